@@ -1,0 +1,193 @@
+"""Tile route map and scanline masks (oracle side; test infrastructure only).
+
+Route map -- "Krea 2 TileMix Attention (FP16/INT8 tiles)", section "What it
+actually patches": every tile of the score matrix is sent to the FP16 or the
+INT8 path by a static map; tiles that read a text key block or write a text
+query row stay FP16, and so does a diagonal band of key blocks around each
+query; the INT8 share counts only the image-image tiles left after that.
+Section "The inputs that matter": pattern ``band`` keeps the diagonal window
+in FP16, ``one`` sends every image tile to INT8, ``zero`` is all FP16.
+
+Readings (the page leaves these open):
+  * a 128-token block is a text block if it holds any text token;
+  * the band is |a - b| <= band_blocks in global block indices;
+  * the number of INT8 tiles is floor(percentage * #candidates) in fp64;
+  * which candidates: the ones with the smallest SplitMix64 key of
+    seed XOR (a << 32 | b), ties broken by (a, b) -- a seeded deterministic pick;
+  * ``one`` ignores band and percentage.
+
+Scanline -- "Krea 2 Scanline Attention", section "What the mask actually is":
+text tokens see everything and are seen by every image token; an image token
+sees image tokens whose grid row is within window // 2 of its own.  Text and
+the image tail are re-padded to multiples of 128 and the padding is masked; the
+block mask is built at 128-token tiles and ``tile_aligned`` admits every valid
+pair inside an active tile.  Section "The settings that matter": the window is
+odd, at most 255.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+TILE = 128
+_M64 = (1 << 64) - 1
+
+
+def splitmix64(x: int) -> int:
+    """One output of SplitMix64 (Steele, Lea and Flood, OOPSLA 2014) from state x.
+
+    The state advances by the golden-ratio increment, then two xor-shift-multiply
+    rounds and a final xor-shift mix it.
+    """
+    z = (x + 0x9E3779B97F4A7C15) & _M64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _M64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _M64
+    return z ^ (z >> 31)
+
+
+def n_blocks(tokens: int) -> int:
+    return (tokens + TILE - 1) // TILE
+
+
+def is_text_block(a: int, text_tokens: int) -> bool:
+    """Block a holds a text token (so every tile in its row and column stays FP16)."""
+    return a * TILE < text_tokens
+
+
+def route_map(tokens: int, text_tokens: int, pattern: str, percentage: float = 0.5,
+              band_blocks: int = 2, seed: int = 0) -> np.ndarray:
+    """uint8 [nb, nb] map over (query block a, key block b): 0 = FP16, 1 = INT8.
+
+    TileMix page, "What it actually patches" and "The inputs that matter".
+    """
+    nb = n_blocks(tokens)
+    r = np.zeros((nb, nb), dtype=np.uint8)
+    if pattern == "zero":
+        return r
+    image = [a for a in range(nb) if not is_text_block(a, text_tokens)]
+    if pattern == "one":
+        for a in image:
+            for b in image:
+                r[a, b] = 1
+        return r
+    if pattern != "band":
+        raise ValueError(f"unknown pattern {pattern!r}")
+    candidates = [(a, b) for a in image for b in image if abs(a - b) > band_blocks]
+    k = math.floor(float(percentage) * len(candidates))
+    seed &= _M64
+    ranked = sorted(candidates, key=lambda ab: (splitmix64(seed ^ ((ab[0] << 32) | ab[1])), ab[0], ab[1]))
+    for a, b in ranked[:k]:
+        r[a, b] = 1
+    return r
+
+
+@dataclass(frozen=True)
+class ScanLayout:
+    """Logical padded token layout for the scanline mask.
+
+    Logical positions: text [0, T), text padding [T, T_pad), image token
+    r * C + c at T_pad + r * C + c, tail padding up to a multiple of 128
+    (Scanline page, "What the mask actually is").
+    """
+
+    text_tokens: int
+    img_rows: int
+    img_cols: int
+
+    @property
+    def t_pad(self) -> int:
+        return n_blocks(self.text_tokens) * TILE
+
+    @property
+    def image_tokens(self) -> int:
+        return self.img_rows * self.img_cols
+
+    @property
+    def length(self) -> int:
+        return n_blocks(self.t_pad + self.image_tokens) * TILE
+
+    def valid(self, t: np.ndarray) -> np.ndarray:
+        t = np.asarray(t)
+        return (t < self.text_tokens) | ((t >= self.t_pad) & (t < self.t_pad + self.image_tokens))
+
+    def physical(self, t: np.ndarray) -> np.ndarray:
+        """Index into the unpadded [text, image] sequence, -1 for padding."""
+        t = np.asarray(t)
+        p = np.where(t < self.text_tokens, t, t - (self.t_pad - self.text_tokens))
+        return np.where(self.valid(t), p, -1)
+
+    def grid_row(self, t: np.ndarray) -> np.ndarray:
+        """Image grid row of a logical image position, -1 elsewhere."""
+        t = np.asarray(t)
+        img = (t >= self.t_pad) & (t < self.t_pad + self.image_tokens)
+        return np.where(img, (t - self.t_pad) // max(self.img_cols, 1), -1)
+
+
+def check_window(window: int) -> None:
+    """Window must be an odd integer in [1, 255] (Scanline page, "The settings that matter")."""
+    if window < 1 or window > 255 or window % 2 == 0:
+        raise ValueError(f"window must be odd in [1, 255], got {window}")
+
+
+def token_rule(lay: ScanLayout, window: int, rows: np.ndarray, cols: np.ndarray) -> np.ndarray:
+    """bool [len(rows), len(cols)]: the scanline rule M(i, j) on logical positions.
+
+    Both tokens valid, and (i is text, or j is text, or their grid rows differ
+    by at most window // 2) -- Scanline page, "What the mask actually is".
+    """
+    rows = np.asarray(rows)
+    cols = np.asarray(cols)
+    vi = lay.valid(rows)[:, None]
+    vj = lay.valid(cols)[None, :]
+    ti = (rows < lay.text_tokens)[:, None]
+    tj = (cols < lay.text_tokens)[None, :]
+    ri = lay.grid_row(rows)[:, None]
+    rj = lay.grid_row(cols)[None, :]
+    near = np.abs(ri - rj) <= window // 2
+    return vi & vj & (ti | tj | near)
+
+
+def block_mask(text_tokens: int, img_rows: int, img_cols: int, window: int,
+               tile_aligned: bool) -> np.ndarray:
+    """uint8 [nb, nb] over logical 128-token tiles: 0 skip, 1 full, 2 partial.
+
+    A tile is active when the token rule admits some pair in it.  Inside an
+    active tile, tile_aligned admits every valid pair, otherwise exactly the
+    rule's pairs.  "Full" means every pair of the tile is admitted (no element
+    masking needed); "partial" means some are not.
+    """
+    check_window(window)
+    lay = ScanLayout(text_tokens, img_rows, img_cols)
+    nb = lay.length // TILE
+    out = np.zeros((nb, nb), dtype=np.uint8)
+    allpos = np.arange(lay.length)
+    valid = lay.valid(allpos)
+    for a in range(nb):
+        rows = allpos[a * TILE:(a + 1) * TILE]
+        m = token_rule(lay, window, rows, allpos)
+        for b in range(nb):
+            sub = m[:, b * TILE:(b + 1) * TILE]
+            if not sub.any():
+                continue
+            if tile_aligned:
+                adm = valid[a * TILE:(a + 1) * TILE][:, None] & valid[b * TILE:(b + 1) * TILE][None, :]
+            else:
+                adm = sub
+            out[a, b] = 1 if adm.all() else 2
+    return out
+
+
+def admitted(lay: ScanLayout, window: int, tile_aligned: bool, rows: np.ndarray,
+             bmask: np.ndarray | None = None) -> np.ndarray:
+    """bool [len(rows), L]: keys each logical query row attends to under the scanline mask."""
+    rows = np.asarray(rows)
+    cols = np.arange(lay.length)
+    m = token_rule(lay, window, rows, cols)
+    if not tile_aligned:
+        return m
+    if bmask is None:
+        bmask = block_mask(lay.text_tokens, lay.img_rows, lay.img_cols, window, True)
+    active = bmask[rows // TILE][:, cols // TILE] != 0
+    return active & lay.valid(rows)[:, None] & lay.valid(cols)[None, :]
