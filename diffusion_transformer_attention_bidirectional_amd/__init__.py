@@ -1,0 +1,241 @@
+"""MI355X (gfx950) joint [text, image] attention for Krea 2 -- Python binding.
+
+Argument marshalling over the C ABI of ``libkrea_attn.so`` (declared in
+include/krea_attn.h); every step of the computation runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current stream only.  If the
+library is not built, every call raises ``KreaAttnError``: there is no other path.
+
+Modes ("Krea 2 TileMix Attention (FP16/INT8 tiles)" and "Krea 2 Scanline Attention"):
+  "dense"     bidirectional softmax attention, GQA resolved in the kernel;
+  "tilemix"   static per-tile FP16/INT8 routing (patterns "zero", "one", "band"),
+              smooth_k mean-centring of K, one running softmax;
+  "scanline"  text global, image tokens see image rows within window // 2.
+``q_chunk`` slices the queries against the full K/V ("LayerStream: Krea2 Chunking").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkrea_attn.so")
+
+ATTN_F16, ATTN_BF16, ATTN_F32 = 0, 1, 2
+MODES = {"dense": 0, "tilemix": 1, "scanline": 2}
+PATTERNS = {"zero": 0, "one": 1, "band": 2}
+STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported dtype", -3: "unsupported shape",
+          -4: "workspace too small", -5: "device error"}
+
+EXPORTS = ("attn_workspace_bytes", "attn_forward", "attn_plan_info_get", "attn_route_map",
+           "attn_block_mask", "attn_quantize", "attn_int8_scores", "attn_mask_row_counts",
+           "attn_status_string", "attn_last_error")
+
+
+class KreaAttnError(RuntimeError):
+    """A status code other than ATTN_OK, or the library missing."""
+
+    def __init__(self, msg: str, status: int | None = None):
+        super().__init__(msg)
+        self.status = status
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("text_tokens", ctypes.c_int32), ("img_rows", ctypes.c_int32),
+        ("img_cols", ctypes.c_int32), ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("mode", ctypes.c_int32), ("pattern", ctypes.c_int32), ("percentage", ctypes.c_double),
+        ("band_blocks", ctypes.c_int32), ("smooth_k", ctypes.c_int32), ("seed", ctypes.c_uint64),
+        ("window", ctypes.c_int32), ("tile_aligned", ctypes.c_int32), ("q_chunk", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class AttnTensor(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("stride_b", ctypes.c_int64), ("stride_t", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64)]
+
+
+class AttnPlanInfo(ctypes.Structure):
+    _fields_ = [("n_blocks", ctypes.c_int32), ("text_blocks", ctypes.c_int32),
+                ("logical_tokens", ctypes.c_int32), ("text_pad", ctypes.c_int32),
+                ("int8_tiles", ctypes.c_int64), ("active_tiles", ctypes.c_int64),
+                ("partial_tiles", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the C-ABI library once; raise KreaAttnError when it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise KreaAttnError(f"{path} is missing: build it with __graft_entry__.build() "
+                            "or python diffusion_transformer_attention_bidirectional_amd/build.py")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    sig = {
+        "attn_workspace_bytes": [P(AttnArgs), P(sz)],
+        "attn_forward": [P(AttnArgs), P(AttnTensor), P(AttnTensor), P(AttnTensor), P(AttnTensor), vp, sz, vp],
+        "attn_plan_info_get": [P(AttnArgs), P(AttnPlanInfo)],
+        "attn_route_map": [P(AttnArgs), vp, i32],
+        "attn_block_mask": [P(AttnArgs), vp, i32],
+        "attn_quantize": [P(AttnArgs), P(AttnTensor), P(AttnTensor), vp, sz, vp, vp, vp, vp, vp, vp],
+        "attn_int8_scores": [P(AttnArgs), P(AttnTensor), P(AttnTensor), vp, sz, vp, i32, vp, vp],
+        "attn_mask_row_counts": [P(AttnArgs), vp, vp],
+    }
+    for name, argtypes in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = argtypes
+        fn.restype = ctypes.c_int32
+    lib.attn_status_string.argtypes = [ctypes.c_int32]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load_library()
+        raise KreaAttnError(f"{lib.attn_status_string(status).decode()}: {lib.attn_last_error().decode()}",
+                            status)
+
+
+def make_args(*, batch=1, heads_q=48, heads_kv=12, head_dim=128, text_tokens=0, img_rows=0, img_cols=0,
+              dtype="bf16", softmax_scale=0.0, mode="dense", pattern="band", percentage=0.5,
+              band_blocks=2, smooth_k=True, seed=0, window=11, tile_aligned=True, q_chunk=0) -> AttnArgs:
+    dt = {"bf16": ATTN_BF16, "f16": ATTN_F16, "f32": ATTN_F32}[dtype] if isinstance(dtype, str) else int(dtype)
+    return AttnArgs(batch, heads_q, heads_kv, head_dim, text_tokens, img_rows, img_cols, dt,
+                    float(softmax_scale), MODES[mode] if isinstance(mode, str) else int(mode),
+                    PATTERNS[pattern] if isinstance(pattern, str) else int(pattern), float(percentage),
+                    band_blocks, 1 if smooth_k else 0, seed & ((1 << 64) - 1), window,
+                    1 if tile_aligned else 0, q_chunk, 0)
+
+
+def _dtype_name(t) -> str:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return "bf16"
+    if t.dtype == torch.float16:
+        return "f16"
+    if t.dtype == torch.float32:
+        return "f32"
+    raise KreaAttnError(f"unsupported dtype {t.dtype}")
+
+
+def _tensor(t) -> AttnTensor:
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise KreaAttnError("tensors must be [B, N, H, head_dim] with head_dim contiguous")
+    return AttnTensor(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _stream_handle(stream, device):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def workspace_bytes(args: AttnArgs) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().attn_workspace_bytes(ctypes.byref(args), ctypes.byref(n)))
+    return n.value
+
+
+def args_for(q, k, *, text_tokens, img_rows=0, img_cols=0, **kw) -> AttnArgs:
+    b, n, hq, d = q.shape
+    hkv = k.shape[2]
+    return make_args(batch=b, heads_q=hq, heads_kv=hkv, head_dim=d, text_tokens=text_tokens,
+                     img_rows=img_rows, img_cols=img_cols, dtype=_dtype_name(q), **kw)
+
+
+def attention(q, k, v, *, text_tokens, img_rows=0, img_cols=0, mode="dense", out=None, workspace=None,
+              stream=None, **kw):
+    """O = attention(q, k, v) on the GPU.  q [B, N, Hq, 128], k/v [B, N, Hkv, 128], bf16 or fp16,
+    N = text_tokens + img_rows * img_cols.  Extra keywords as in make_args().  Asynchronous on
+    the current (or given) stream."""
+    import torch
+    args = args_for(q, k, text_tokens=text_tokens, img_rows=img_rows, img_cols=img_cols, mode=mode, **kw)
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    nbytes = workspace_bytes(args)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wlen = workspace.numel() if workspace is not None else 0
+    _check(load_library().attn_forward(ctypes.byref(args), ctypes.byref(_tensor(q)), ctypes.byref(_tensor(k)),
+                                       ctypes.byref(_tensor(v)), ctypes.byref(_tensor(out)), wptr, wlen,
+                                       _stream_handle(stream, q.device)))
+    return out
+
+
+# ---------------------------------------------------------------- host-only plan views
+def plan_info(args: AttnArgs) -> dict:
+    info = AttnPlanInfo()
+    _check(load_library().attn_plan_info_get(ctypes.byref(args), ctypes.byref(info)))
+    return {f: getattr(info, f) for f, _ in AttnPlanInfo._fields_}
+
+
+def route_map(args: AttnArgs) -> np.ndarray:
+    nb = plan_info(args)["n_blocks"]
+    out = np.zeros((nb, nb), dtype=np.uint8)
+    _check(load_library().attn_route_map(ctypes.byref(args), out.ctypes.data, nb))
+    return out
+
+
+def block_mask(args: AttnArgs) -> np.ndarray:
+    nb = plan_info(args)["n_blocks"]
+    out = np.zeros((nb, nb), dtype=np.uint8)
+    _check(load_library().attn_block_mask(ctypes.byref(args), out.ctypes.data, nb))
+    return out
+
+
+# ---------------------------------------------------------------- device debug views
+def quantize(q, k, args: AttnArgs, stream=None) -> dict:
+    """smooth_k mean, INT8 codes and scales of K and Q as the attention call computes them."""
+    import torch
+    dev = q.device
+    nb = plan_info(args)["n_blocks"]
+    b, hq, hkv = args.batch, args.heads_q, args.heads_kv
+    ws = torch.empty(workspace_bytes(args), dtype=torch.uint8, device=dev)
+    res = {
+        "k_mean": torch.empty((b, hkv, 128), dtype=torch.float32, device=dev),
+        "k_codes": torch.empty((b, hkv, nb, 128, 128), dtype=torch.int8, device=dev),
+        "k_scale": torch.empty((b, hkv, nb), dtype=torch.float32, device=dev),
+        "q_codes": torch.empty((b, hq, nb, 128, 128), dtype=torch.int8, device=dev),
+        "q_scale": torch.empty((b, hq, nb), dtype=torch.float32, device=dev),
+    }
+    _check(load_library().attn_quantize(
+        ctypes.byref(args), ctypes.byref(_tensor(q)), ctypes.byref(_tensor(k)), ws.data_ptr(), ws.numel(),
+        res["k_mean"].data_ptr(), res["k_codes"].data_ptr(), res["k_scale"].data_ptr(),
+        res["q_codes"].data_ptr(), res["q_scale"].data_ptr(), _stream_handle(stream, dev)))
+    return res
+
+
+def int8_scores(q, k, args: AttnArgs, tiles, stream=None):
+    """INT32 q8 . k8 of tiles [(b, h, query block, key block), ...] -> int32 [n, 128, 128]."""
+    import torch
+    dev = q.device
+    t = torch.as_tensor(np.asarray(tiles, dtype=np.int32).reshape(-1, 4), device=dev).contiguous()
+    out = torch.empty((t.shape[0], 128, 128), dtype=torch.int32, device=dev)
+    ws = torch.empty(workspace_bytes(args), dtype=torch.uint8, device=dev)
+    _check(load_library().attn_int8_scores(
+        ctypes.byref(args), ctypes.byref(_tensor(q)), ctypes.byref(_tensor(k)), ws.data_ptr(), ws.numel(),
+        t.data_ptr(), t.shape[0], out.data_ptr(), _stream_handle(stream, dev)))
+    return out
+
+
+def mask_row_counts(args: AttnArgs, device="cuda", stream=None):
+    """Keys admitted per logical query row, as the attention kernel's mask evaluates them."""
+    import torch
+    n = plan_info(args)["logical_tokens"]
+    out = torch.empty(n, dtype=torch.int32, device=device)
+    _check(load_library().attn_mask_row_counts(ctypes.byref(args), out.data_ptr(),
+                                               _stream_handle(stream, torch.device(device))))
+    return out

@@ -1,0 +1,359 @@
+// C ABI: validation, plan cache, launch sequencing.  Declarations and the meaning of
+// every argument are in include/krea_attn.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <list>
+#include <memory>
+#include <mutex>
+#include <string>
+
+#include "kernels.hpp"
+#include "krea_attn.h"
+#include "plan.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+attn_status fail(attn_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+// A plan plus its device copy.  Device layout: route map [nb * nb] (TileMix) or
+// row_ptr [nb + 1] int32 then cols [nnz] int32 (scanline).
+struct DevicePlan {
+  std::string key;
+  int device = -1;
+  krea::Plan plan;
+  unsigned char* dmem = nullptr;
+  size_t route_off = 0, row_ptr_off = 0, cols_off = 0;
+  ~DevicePlan() {
+    if (dmem) {
+      int cur = 0;
+      if (hipGetDevice(&cur) == hipSuccess && cur != device) (void)hipSetDevice(device);
+      (void)hipDeviceSynchronize();  // calls still in flight may read this plan
+      (void)hipFree(dmem);
+      if (cur != device) (void)hipSetDevice(cur);
+    }
+  }
+};
+
+constexpr size_t kMaxPlans = 8;  // the Scanline page keeps at most eight masks cached
+std::mutex g_mu;
+std::list<std::shared_ptr<DevicePlan>> g_cache;  // most recent first
+
+attn_status get_plan(const attn_args& a, std::shared_ptr<DevicePlan>* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(ATTN_ERR_DEVICE, "hipGetDevice failed (no GPU?)");
+  const std::string key = krea::plan_key(a);
+  std::lock_guard<std::mutex> lock(g_mu);
+  for (auto it = g_cache.begin(); it != g_cache.end(); ++it) {
+    if ((*it)->device == dev && (*it)->key == key) {
+      g_cache.splice(g_cache.begin(), g_cache, it);
+      *out = g_cache.front();
+      return ATTN_OK;
+    }
+  }
+  auto dp = std::make_shared<DevicePlan>();
+  dp->key = key;
+  dp->device = dev;
+  dp->plan = krea::build_plan(a);
+  const krea::Plan& p = dp->plan;
+  size_t bytes = 0;
+  dp->route_off = bytes;
+  bytes += (p.route.size() + 255) & ~(size_t)255;
+  dp->row_ptr_off = bytes;
+  bytes += (p.row_ptr.size() * 4 + 255) & ~(size_t)255;
+  dp->cols_off = bytes;
+  bytes += (p.cols.size() * 4 + 255) & ~(size_t)255;
+  if (bytes == 0) bytes = 256;
+  if (hipMalloc((void**)&dp->dmem, bytes) != hipSuccess) {
+    dp->dmem = nullptr;
+    return fail(ATTN_ERR_DEVICE, "hipMalloc of the plan failed");
+  }
+  hipError_t e = hipSuccess;
+  if (!p.route.empty()) e = hipMemcpy(dp->dmem + dp->route_off, p.route.data(), p.route.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess && !p.row_ptr.empty())
+    e = hipMemcpy(dp->dmem + dp->row_ptr_off, p.row_ptr.data(), p.row_ptr.size() * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess && !p.cols.empty())
+    e = hipMemcpy(dp->dmem + dp->cols_off, p.cols.data(), p.cols.size() * 4, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, std::string("plan upload failed: ") + hipGetErrorString(e));
+  if (std::getenv("KREA_ATTN_LOG")) {
+    std::fprintf(stderr, "[krea_attn] plan built: mode %d, %d blocks, %lld INT8 tiles, %lld active, %lld partial\n",
+                 a.mode, p.lay.nb, (long long)p.int8_tiles, (long long)p.active_tiles, (long long)p.partial_tiles);
+  }
+  g_cache.push_front(dp);
+  while (g_cache.size() > kMaxPlans) g_cache.pop_back();
+  *out = dp;
+  return ATTN_OK;
+}
+
+attn_status check_args(const attn_args* a) {
+  if (!a) return fail(ATTN_ERR_INVALID_ARG, "args is NULL");
+  std::string err;
+  const attn_status s = krea::validate_args(*a, err);
+  if (s != ATTN_OK) return fail(s, err);
+  return ATTN_OK;
+}
+
+attn_status check_tensor(const attn_tensor* t, const char* name) {
+  if (!t || !t->ptr) return fail(ATTN_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  if (((uintptr_t)t->ptr & 15) != 0) return fail(ATTN_ERR_INVALID_ARG, std::string(name) + " must be 16-byte aligned");
+  if ((t->stride_b & 7) || (t->stride_t & 7) || (t->stride_h & 7))
+    return fail(ATTN_ERR_INVALID_ARG, std::string(name) + " strides must be multiples of 8 elements");
+  if (t->stride_b < 0 || t->stride_t < 0 || t->stride_h < 0)
+    return fail(ATTN_ERR_INVALID_ARG, std::string(name) + " strides must be >= 0");
+  return ATTN_OK;
+}
+
+krea::TensorRef ref(const attn_tensor* t) { return krea::TensorRef{t->ptr, t->stride_b, t->stride_t, t->stride_h}; }
+
+float scale_of(const attn_args& a) {
+  return a.softmax_scale > 0.0f ? a.softmax_scale : (float)(1.0 / std::sqrt((double)a.head_dim));
+}
+
+krea::AttnParams make_params(const attn_args& a, const DevicePlan* dp) {
+  krea::AttnParams p;
+  std::memset(&p, 0, sizeof(p));
+  const krea::Layout& l = dp->plan.lay;
+  p.batch = a.batch;
+  p.heads_q = a.heads_q;
+  p.heads_kv = a.heads_kv;
+  p.group = a.heads_q / a.heads_kv;
+  p.n = l.n;
+  p.text = l.text;
+  p.t_pad = l.t_pad;
+  p.image = l.image;
+  p.cols = l.cols;
+  p.cols_magic = (uint32_t)(0xFFFFFFFFu / (uint32_t)l.cols);
+  p.length = l.length;
+  p.nb = l.nb;
+  p.q_begin = 0;
+  p.q_end = l.length;
+  p.scale_log2 = (float)((double)scale_of(a) * 1.4426950408889634);
+  p.half_window = a.window / 2;
+  p.tile_aligned = a.tile_aligned ? 1 : 0;
+  p.smooth_k = a.smooth_k ? 1 : 0;
+  if (!dp->plan.route.empty()) p.route = dp->dmem + dp->route_off;
+  if (!dp->plan.row_ptr.empty()) p.row_ptr = (const int32_t*)(dp->dmem + dp->row_ptr_off);
+  if (!dp->plan.cols.empty()) p.cols_list = (const int32_t*)(dp->dmem + dp->cols_off);
+  return p;
+}
+
+krea::QuantParams make_quant(const attn_args& a, const attn_tensor* q, const attn_tensor* k, unsigned char* ws) {
+  const krea::WorkspaceLayout w = krea::workspace_layout(a);
+  const krea::Layout l = krea::make_layout(a);
+  krea::QuantParams qp;
+  std::memset(&qp, 0, sizeof(qp));
+  qp.q = ref(q);
+  qp.k = ref(k);
+  qp.batch = a.batch;
+  qp.heads_q = a.heads_q;
+  qp.heads_kv = a.heads_kv;
+  qp.n = l.n;
+  qp.text = l.text;
+  qp.nb = l.nb;
+  qp.smooth_k = a.smooth_k ? 1 : 0;
+  qp.bf16 = a.dtype == ATTN_BF16;
+  qp.k_part = (double*)(ws + w.k_part);
+  qp.k_mean = (float*)(ws + w.k_mean);
+  qp.k_codes = (int8_t*)(ws + w.k_codes);
+  qp.k_scale = (float*)(ws + w.k_scale);
+  qp.q_inv = (float*)(ws + w.q_inv);
+  qp.q_scale = (float*)(ws + w.q_scale);
+  return qp;
+}
+
+attn_status hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_workspace_bytes(const attn_args* args, size_t* bytes) {
+  attn_status s = check_args(args);
+  if (s != ATTN_OK) return s;
+  if (!bytes) return fail(ATTN_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = krea::workspace_layout(*args).total;
+  g_err.clear();
+  return ATTN_OK;
+}
+
+attn_status attn_forward(const attn_args* args, const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                         const attn_tensor* o, void* workspace, size_t workspace_bytes, void* stream) {
+  attn_status s = check_args(args);
+  if (s != ATTN_OK) return s;
+  if ((s = check_tensor(q, "q")) || (s = check_tensor(k, "k")) || (s = check_tensor(v, "v")) ||
+      (s = check_tensor(o, "o")))
+    return s;
+  const attn_args& a = *args;
+  const krea::WorkspaceLayout w = krea::workspace_layout(a);
+  if (w.total > 0 && (!workspace || workspace_bytes < w.total))
+    return fail(ATTN_ERR_WORKSPACE, "workspace smaller than attn_workspace_bytes()");
+  if (workspace && ((uintptr_t)workspace & 255)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  std::shared_ptr<DevicePlan> dp;
+  if ((s = get_plan(a, &dp)) != ATTN_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  krea::AttnParams p = make_params(a, dp.get());
+  p.q = ref(q);
+  p.k = ref(k);
+  p.v = ref(v);
+  p.o = o->ptr;
+  p.o_sb = o->stride_b;
+  p.o_st = o->stride_t;
+  p.o_sh = o->stride_h;
+  const bool bf16 = a.dtype == ATTN_BF16;
+  if (a.mode == ATTN_TILEMIX) {
+    if (dp->plan.int8_tiles > 0) {
+      const krea::QuantParams qp = make_quant(a, q, k, (unsigned char*)workspace);
+      if ((s = hip_check(krea::launch_quant(qp, st), "quantiser launch")) != ATTN_OK) return s;
+      p.k_mean = qp.k_mean;
+      p.k_codes = qp.k_codes;
+      p.k_scale = qp.k_scale;
+      p.q_inv = qp.q_inv;
+      p.q_scale = qp.q_scale;
+    } else {
+      p.route = nullptr;  // all FP16: the TileMix kernel never looks at INT8 state
+    }
+  }
+  const int length = dp->plan.lay.length;
+  const int chunk = a.q_chunk > 0 ? a.q_chunk : length;
+  const int mode = a.mode;
+  for (int q0 = 0; q0 < length; q0 += chunk) {
+    p.q_begin = q0;
+    p.q_end = std::min(length, q0 + chunk);
+    if ((s = hip_check(krea::launch_attention(p, mode, bf16, st), "attention launch")) != ATTN_OK) return s;
+  }
+  g_err.clear();
+  return ATTN_OK;
+}
+
+attn_status attn_plan_info_get(const attn_args* args, attn_plan_info* out) {
+  attn_status s = check_args(args);
+  if (s != ATTN_OK) return s;
+  if (!out) return fail(ATTN_ERR_INVALID_ARG, "out is NULL");
+  const krea::Plan p = krea::build_plan(*args);
+  out->n_blocks = p.lay.nb;
+  out->text_blocks = (p.lay.text + krea::kTile - 1) / krea::kTile;
+  out->logical_tokens = p.lay.length;
+  out->text_pad = p.lay.t_pad;
+  out->int8_tiles = p.int8_tiles;
+  out->active_tiles = p.active_tiles;
+  out->partial_tiles = p.partial_tiles;
+  g_err.clear();
+  return ATTN_OK;
+}
+
+attn_status attn_route_map(const attn_args* args, uint8_t* out, int32_t nb) {
+  attn_status s = check_args(args);
+  if (s != ATTN_OK) return s;
+  if (args->mode != ATTN_TILEMIX) return fail(ATTN_ERR_INVALID_ARG, "route map exists for ATTN_TILEMIX only");
+  const krea::Layout l = krea::make_layout(*args);
+  if (!out || nb != l.nb) return fail(ATTN_ERR_INVALID_ARG, "out is NULL or nb does not match the plan");
+  const std::vector<uint8_t> r = krea::build_route_map(*args, l, nullptr);
+  std::memcpy(out, r.data(), r.size());
+  g_err.clear();
+  return ATTN_OK;
+}
+
+attn_status attn_block_mask(const attn_args* args, uint8_t* out, int32_t nb) {
+  attn_status s = check_args(args);
+  if (s != ATTN_OK) return s;
+  if (args->mode != ATTN_SCANLINE) return fail(ATTN_ERR_INVALID_ARG, "block mask exists for ATTN_SCANLINE only");
+  const krea::Layout l = krea::make_layout(*args);
+  if (!out || nb != l.nb) return fail(ATTN_ERR_INVALID_ARG, "out is NULL or nb does not match the plan");
+  const std::vector<uint8_t> m = krea::build_block_mask(*args, l);
+  std::memcpy(out, m.data(), m.size());
+  g_err.clear();
+  return ATTN_OK;
+}
+
+attn_status attn_quantize(const attn_args* args, const attn_tensor* q, const attn_tensor* k, void* workspace,
+                          size_t workspace_bytes, float* k_mean, int8_t* k_codes, float* k_scale, int8_t* q_codes,
+                          float* q_scale, void* stream) {
+  attn_status s = check_args(args);
+  if (s != ATTN_OK) return s;
+  if (args->mode != ATTN_TILEMIX) return fail(ATTN_ERR_INVALID_ARG, "attn_quantize needs mode ATTN_TILEMIX");
+  if ((s = check_tensor(q, "q")) || (s = check_tensor(k, "k"))) return s;
+  const krea::WorkspaceLayout w = krea::workspace_layout(*args);
+  if (!workspace || workspace_bytes < w.total) return fail(ATTN_ERR_WORKSPACE, "workspace too small");
+  hipStream_t st = (hipStream_t)stream;
+  const krea::QuantParams qp = make_quant(*args, q, k, (unsigned char*)workspace);
+  if ((s = hip_check(krea::launch_quant(qp, st), "quantiser launch")) != ATTN_OK) return s;
+  const size_t bk = (size_t)args->batch * args->heads_kv, bq = (size_t)args->batch * args->heads_q;
+  const size_t nb = (size_t)qp.nb;
+  if (k_mean && (s = hip_check(hipMemcpyAsync(k_mean, qp.k_mean, bk * 128 * 4, hipMemcpyDeviceToDevice, st), "copy")))
+    return s;
+  if (k_codes &&
+      (s = hip_check(hipMemcpyAsync(k_codes, qp.k_codes, bk * nb * 128 * 128, hipMemcpyDeviceToDevice, st), "copy")))
+    return s;
+  if (k_scale && (s = hip_check(hipMemcpyAsync(k_scale, qp.k_scale, bk * nb * 4, hipMemcpyDeviceToDevice, st), "copy")))
+    return s;
+  if (q_scale && (s = hip_check(hipMemcpyAsync(q_scale, qp.q_scale, bq * nb * 4, hipMemcpyDeviceToDevice, st), "copy")))
+    return s;
+  if (q_codes && (s = hip_check(krea::launch_q_codes(qp, q_codes, st), "q codes launch"))) return s;
+  g_err.clear();
+  return ATTN_OK;
+}
+
+attn_status attn_int8_scores(const attn_args* args, const attn_tensor* q, const attn_tensor* k, void* workspace,
+                             size_t workspace_bytes, const int32_t* tiles, int32_t n_tiles, int32_t* out,
+                             void* stream) {
+  attn_status s = check_args(args);
+  if (s != ATTN_OK) return s;
+  if (args->mode != ATTN_TILEMIX) return fail(ATTN_ERR_INVALID_ARG, "attn_int8_scores needs mode ATTN_TILEMIX");
+  if ((s = check_tensor(q, "q")) || (s = check_tensor(k, "k"))) return s;
+  if (n_tiles < 0 || (n_tiles > 0 && (!tiles || !out))) return fail(ATTN_ERR_INVALID_ARG, "bad tile list");
+  const krea::WorkspaceLayout w = krea::workspace_layout(*args);
+  if (!workspace || workspace_bytes < w.total) return fail(ATTN_ERR_WORKSPACE, "workspace too small");
+  std::shared_ptr<DevicePlan> dp;
+  if ((s = get_plan(*args, &dp)) != ATTN_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const krea::QuantParams qp = make_quant(*args, q, k, (unsigned char*)workspace);
+  if ((s = hip_check(krea::launch_quant(qp, st), "quantiser launch")) != ATTN_OK) return s;
+  krea::AttnParams p = make_params(*args, dp.get());
+  p.q = ref(q);
+  p.k = ref(k);
+  p.k_codes = qp.k_codes;
+  p.q_inv = qp.q_inv;
+  if ((s = hip_check(krea::launch_int8_scores(p, tiles, n_tiles, out, args->dtype == ATTN_BF16, st), "launch")))
+    return s;
+  g_err.clear();
+  return ATTN_OK;
+}
+
+attn_status attn_mask_row_counts(const attn_args* args, int32_t* out, void* stream) {
+  attn_status s = check_args(args);
+  if (s != ATTN_OK) return s;
+  if (!out) return fail(ATTN_ERR_INVALID_ARG, "out is NULL");
+  std::shared_ptr<DevicePlan> dp;
+  if ((s = get_plan(*args, &dp)) != ATTN_OK) return s;
+  const krea::AttnParams p = make_params(*args, dp.get());
+  if ((s = hip_check(krea::launch_mask_counts(p, args->mode, out, (hipStream_t)stream), "launch"))) return s;
+  g_err.clear();
+  return ATTN_OK;
+}
+
+const char* attn_status_string(attn_status status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
+    case ATTN_ERR_SHAPE: return "unsupported shape";
+    case ATTN_ERR_WORKSPACE: return "workspace too small";
+    case ATTN_ERR_DEVICE: return "device error";
+    default: return "unknown status";
+  }
+}
+
+const char* attn_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,787 @@
+// HIP kernels for gfx950 (MI355X): TileMix quantiser, fused joint attention, debug views.
+//
+// Fused attention ("Krea 2 TileMix Attention (FP16/INT8 tiles)", "What it actually
+// patches"): bidirectional online-softmax attention; GQA is resolved in the kernel --
+// one workgroup owns 64 query tokens of the 4 query heads that share one KV head
+// (one wave per head), so each K/V tile is staged once in LDS and read by all four.
+//
+// Per wave, per step of 64 keys (all matrix products on MFMA 32x32 tiles):
+//   S^T[key, q] = K Q^T            bf16/f16 MFMA (32x32x16), or i8 MFMA (32x32x32) on
+//                                  INT8-routed tiles, int32 accumulate
+//   online softmax per query       each lane owns one query column of S^T, so the row
+//                                  max and sum stay in the lane (one swap with lane^32)
+//   O^T[d, q] += V^T P^T           bf16/f16 MFMA; P^T is the S^T accumulator converted
+//                                  in place; V^T fragments come from the row-major V
+//                                  tile through LDS transpose reads
+// K and V tiles move HBM -> LDS by DMA (global_load_lds), double buffered.
+//
+// Hardware facts this file relies on (checked on gfx950):
+//   * MFMA 32x32 result: lane l holds column l % 32 and, in register r, row
+//     8*(r/4) + 4*(l/32) + r%4 (f32 and i32 results alike);
+//   * ds_read_tr16_b64: inside each group of 16 lanes, result lane i receives element
+//     i % 4 of the 8 bytes loaded by lanes i/4 + 4k of the group, k = 0..3;
+//   * global_load_lds (16 B): lane L writes LDS bytes [base + 16 L, +16).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.hpp"
+
+namespace krea {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kModeDense = 0, kModeTileMix = 1, kModeScan = 2;
+constexpr int QT = 64;          // query tokens per workgroup
+constexpr int KT = 64;          // keys per step
+constexpr int TILE_BYTES = KT * 256;     // one 64 x 128 bf16 tile
+constexpr int V_OFF = TILE_BYTES;        // V tile after K in a stage
+constexpr int STAGE = 2 * TILE_BYTES;    // bytes of LDS per pipeline stage
+constexpr float TAU = 8.0f;     // rescale O only when the running max grows by > 2^8
+
+// ---------------------------------------------------------------- layout helpers
+template <int MODE>
+__device__ __forceinline__ bool tok_valid(const AttnParams& p, int t) {
+  if (MODE != kModeScan) return t < p.n;
+  return t < p.text || (t >= p.t_pad && t < p.t_pad + p.image);
+}
+template <int MODE>
+__device__ __forceinline__ int tok_phys(const AttnParams& p, int t) {
+  if (MODE != kModeScan) return t;
+  return t < p.text ? t : t - (p.t_pad - p.text);
+}
+// grid row of a logical image position: floor((t - t_pad) / cols), exact
+__device__ __forceinline__ int grid_row(const AttnParams& p, int t) {
+  const uint32_t n = (uint32_t)(t - p.t_pad);
+  uint32_t q = __umulhi(n, p.cols_magic);
+  if ((q + 1) * (uint32_t)p.cols <= n) ++q;
+  return (int)q;
+}
+
+// Query-side facts a partial tile's element mask needs.
+struct QInfo {
+  bool valid, text;
+  int row;
+};
+template <int MODE>
+__device__ __forceinline__ QInfo query_info(const AttnParams& p, int t) {
+  QInfo qi;
+  qi.valid = t < p.q_end && tok_valid<MODE>(p, t);
+  qi.text = t < p.text;
+  qi.row = (MODE == kModeScan && qi.valid && !qi.text) ? grid_row(p, t) : -1;
+  return qi;
+}
+// Element mask of a partial tile: key validity, plus the scanline row rule
+// ("Krea 2 Scanline Attention", "What the mask actually is").
+template <int MODE>
+__device__ __forceinline__ bool admit(const AttnParams& p, const QInfo& qi, int j) {
+  if (!tok_valid<MODE>(p, j)) return false;
+  if (MODE != kModeScan) return true;
+  if (!qi.valid) return false;
+  if (p.tile_aligned || qi.text || j < p.text) return true;
+  return abs(qi.row - grid_row(p, j)) <= p.half_window;
+}
+
+// One step of 64 keys: logical start, whether it needs element masking, and its route.
+struct StepInfo {
+  int k0;
+  bool partial, int8;
+};
+template <int MODE>
+__device__ __forceinline__ StepInfo step_info(const AttnParams& p, int qa, int e0, int i) {
+  StepInfo s;
+  int kb;
+  if (MODE == kModeScan) {
+    const int e = p.cols_list[e0 + (i >> 1)];
+    kb = e & 0xffff;
+    s.partial = (e >> 16) != 0;
+  } else {
+    kb = i >> 1;
+  }
+  s.k0 = kb * 128 + (i & 1) * KT;
+  if (MODE != kModeScan) s.partial = s.k0 + KT > p.n;
+  s.int8 = (MODE == kModeTileMix) && p.route != nullptr && p.route[qa * p.nb + kb] != 0;
+  return s;
+}
+template <int MODE>
+__device__ __forceinline__ int step_count(const AttnParams& p, int qa, int* e0) {
+  if (MODE == kModeScan) {
+    *e0 = p.row_ptr[qa];
+    return 2 * (p.row_ptr[qa + 1] - *e0);
+  }
+  *e0 = 0;
+  return 2 * p.nb;
+}
+
+// ---------------------------------------------------------------- LDS layouts
+// bf16/f16 tiles (K and V): 64 rows x 256 B, row-major, 16-byte chunks XOR-swizzled by
+// a bijection of the row's low 4 bits.  Conflict-free for both the K fragment reads
+// (16 consecutive rows, one chunk) and the V transpose reads (4 consecutive rows,
+// 4 consecutive chunks).
+__device__ __forceinline__ int swz16(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+__device__ __forceinline__ int off256(int row, int chunk) { return row * 256 + ((chunk ^ swz16(row)) << 4); }
+// INT8 K tile: 64 rows x 128 B; rows of equal parity spread over the 8 chunk slots.
+__device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int off128(int row, int chunk) { return row * 128 + ((chunk ^ swz8(row)) << 4); }
+// Channel chunk (8 channels) a lane holds in k-step s of the bf16 Q K^T product.  Any
+// bijection works if Q and K agree; this one makes two consecutive steps cover 16
+// contiguous channels per lane, so the INT8 Q codes built from them line up with the
+// natural 16-byte chunks of the INT8 K rows.
+__device__ __forceinline__ int qk_chunk(int s, int lh) { return 4 * (s >> 1) + 2 * lh + (s & 1); }
+
+__device__ __forceinline__ lds_void* as_lds(unsigned char* p) { return (lds_void*)p; }
+
+// HBM -> LDS for one step, by DMA; 16 bytes per lane per instruction, 1 KB per
+// instruction; each wave moves a quarter of the tiles.  Padding and out-of-range
+// keys read row 0 (finite data; their probabilities are zero).
+template <int MODE, bool WITH_V = true>
+__device__ __forceinline__ void dma_stage(const AttnParams& p, int b, int g, const StepInfo& s,
+                                          unsigned char* stage, int wave, int lane) {
+  const uint16_t* kbase = (const uint16_t*)p.k.ptr + (int64_t)b * p.k.sb + (int64_t)g * p.k.sh;
+  const uint16_t* vbase = (const uint16_t*)p.v.ptr + (int64_t)b * p.v.sb + (int64_t)g * p.v.sh;
+#pragma unroll
+  for (int i = 0; i < (WITH_V || !s.int8 ? 4 : 0); ++i) {
+    const int n = wave * 4 + i;
+    const int row = 4 * n + (lane >> 4);
+    const int c = (lane & 15) ^ swz16(row);
+    const int t = s.k0 + row;
+    const int ph = tok_valid<MODE>(p, t) ? tok_phys<MODE>(p, t) : 0;
+    if (!s.int8)
+      __builtin_amdgcn_global_load_lds(kbase + (int64_t)ph * p.k.st + c * 8, as_lds(stage + n * 1024), 16, 0, 0);
+    if (WITH_V)
+      __builtin_amdgcn_global_load_lds(vbase + (int64_t)ph * p.v.st + c * 8, as_lds(stage + V_OFF + n * 1024), 16,
+                                       0, 0);
+  }
+  if (MODE == kModeTileMix && s.int8) {
+    const int8_t* kc = p.k_codes + (((int64_t)b * p.heads_kv + g) * p.nb + (s.k0 >> 7)) * (128 * 128) +
+                       (s.k0 & 127) * 128;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int n = wave * 2 + i;
+      const int row = 8 * n + (lane >> 3);
+      const int c = (lane & 7) ^ swz8(row);
+      __builtin_amdgcn_global_load_lds(kc + row * 128 + c * 16, as_lds(stage + n * 1024), 16, 0, 0);
+    }
+  }
+}
+
+// V^T fragment (A operand of O^T += V^T P^T) for 32 channels 32 db .. and the 16 keys
+// of k-step (kb, k2): two transpose reads of 4 keys each, matching the key order of the
+// P^T B operand taken from the S^T accumulator (keys 16 k2 + 8 half + 4 (l/32) + 0..3).
+__device__ __forceinline__ uint4 v_frag(const unsigned char* vbuf, int db, int kb, int k2, int lane) {
+  const int key = 32 * kb + 16 * k2 + 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int c = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int within = 8 * (lane & 1);
+  unsigned char* base = (unsigned char*)vbuf;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off256(key, c) + within));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off256(key + 8, c) + within));
+  const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+  return make_uint4(l2.x, l2.y, h2.x, h2.y);
+}
+
+// ---------------------------------------------------------------- MFMA wrappers
+template <bool BF16>
+__device__ __forceinline__ f32x16 mma16(uint4 a, uint4 b, f32x16 c);
+template <>
+__device__ __forceinline__ f32x16 mma16<true>(uint4 a, uint4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x16 mma16<false>(uint4 a, uint4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                0);
+}
+__device__ __forceinline__ i32x16 mma8(uint4 a, uint4 b, i32x16 c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+}
+
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if (BF16) {
+    bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    f16x2 v = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+}
+template <bool BF16>
+__device__ __forceinline__ float elem_to_f32(uint16_t bits) {
+  if (BF16) return __uint_as_float((uint32_t)bits << 16);
+  return (float)__builtin_bit_cast(_Float16, bits);
+}
+
+// Symmetric INT8 code of one value: clamp(rint(x * inv), -127, 127), the product a
+// single correctly rounded fp32 multiply, rint = round half to even.
+__device__ __forceinline__ int quant8(float x, float inv) {
+  float y = rintf(__fmul_rn(x, inv));
+  y = fminf(fmaxf(y, -127.0f), 127.0f);
+  return (int)y;
+}
+template <bool BF16>
+__device__ __forceinline__ uint32_t quant4(uint32_t lo2, uint32_t hi2, float inv) {
+  const int c0 = quant8(elem_to_f32<BF16>(lo2 & 0xffff), inv);
+  const int c1 = quant8(elem_to_f32<BF16>(lo2 >> 16), inv);
+  const int c2 = quant8(elem_to_f32<BF16>(hi2 & 0xffff), inv);
+  const int c3 = quant8(elem_to_f32<BF16>(hi2 >> 16), inv);
+  return (uint32_t)(c0 & 255) | ((uint32_t)(c1 & 255) << 8) | ((uint32_t)(c2 & 255) << 16) |
+         ((uint32_t)(c3 & 255) << 24);
+}
+// INT8 B operand of k-step s' (16 contiguous channels) from the Q fragments of
+// bf16 k-steps 2s' and 2s'+1.
+template <bool BF16>
+__device__ __forceinline__ uint4 make_q8(const uint4& a, const uint4& b, float inv) {
+  return make_uint4(quant4<BF16>(a.x, a.y, inv), quant4<BF16>(a.z, a.w, inv), quant4<BF16>(b.x, b.y, inv),
+                    quant4<BF16>(b.z, b.w, inv));
+}
+
+// Q fragments of one 32-query block: lane (lq, lh) holds query t's channel chunk
+// qk_chunk(s, lh) for s = 0..7 (the B operand of K Q^T).
+template <int MODE>
+__device__ __forceinline__ void load_q_frags(const AttnParams& p, int b, int h, int t, uint4 (&qf)[8]) {
+  const int lh = (threadIdx.x & 63) >> 5;
+  const bool ok = t < p.q_end && tok_valid<MODE>(p, t);
+  const uint16_t* src = (const uint16_t*)p.q.ptr + (int64_t)b * p.q.sb +
+                        (int64_t)tok_phys<MODE>(p, ok ? t : 0) * p.q.st + (int64_t)h * p.q.sh;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) qf[s] = ok ? *(const uint4*)(src + 8 * qk_chunk(s, lh)) : make_uint4(0, 0, 0, 0);
+}
+
+// Workgroup -> (query tile, head group, batch).  The hardware deals workgroups to the
+// 8 XCDs round robin; this remap gives each XCD a contiguous range of tiles, so the
+// workgroups sharing one KV head (and its K/V in that XCD's L2) run on the same XCD.
+__device__ __forceinline__ void tile_coords(int n_qtiles, int n_hg, int* qt, int* hg, int* b) {
+  const int total = gridDim.x;
+  const int L = blockIdx.x;
+  const int xcd = L & 7, idx = L >> 3;
+  const int per = total >> 3, rem = total & 7;
+  const int Lp = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+  *qt = Lp % n_qtiles;
+  const int rest = Lp / n_qtiles;
+  *hg = rest % n_hg;
+  *b = rest / n_hg;
+}
+
+// ---------------------------------------------------------------- fused attention
+// Per-wave state carried across steps.
+struct WaveState {
+  f32x16 O[4][2];  // O^T accumulators: 4 channel blocks x 2 query blocks
+  float m[2], l[2];
+};
+
+// One step of 64 keys on the current LDS stage, while the DMA for the next step fills
+// the other stage.  The two stages are separate restrict-qualified pointers so the
+// compiler knows the DMA cannot alias the reads and does not wait for it here.
+template <bool BF16, int MODE>
+__device__ __forceinline__ void attn_step(const AttnParams& p, const unsigned char* __restrict__ buf,
+                                          unsigned char* __restrict__ nbuf, const StepInfo& cur,
+                                          const StepInfo& nxt, bool has_next, int b, int g, int wave, int lane,
+                                          const uint4 (&qf)[2][8], const uint4 (&q8f)[2][4],
+                                          const QInfo (&qinfo)[2], const float (&qadd)[2], float sq_l2,
+                                          WaveState& ws) {
+  const int lq = lane & 31, lh = lane >> 5;
+  if (has_next) dma_stage<MODE>(p, b, g, nxt, nbuf, wave, lane);
+  f32x16 (&O)[4][2] = ws.O;
+  float (&m)[2] = ws.m;
+  float (&l)[2] = ws.l;
+  // Two sub-blocks of 32 keys; within each, K and V fragments are shared by both
+  // 32-query blocks of the wave.
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    // ---- scores S^T[key, q] for 32 keys x 2 query blocks of 32
+    f32x16 S[2];
+    float mul, add[2];
+    if (MODE == kModeTileMix && cur.int8) {
+      i32x16 Si[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Si[qb][r] = 0;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint4 a = *(const uint4*)(buf + off128(32 * kb + lq, 2 * s + lh));
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) Si[qb] = mma8(a, q8f[qb][s], Si[qb]);
+      }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[qb][r] = (float)Si[qb][r];
+      mul = sq_l2 * p.k_scale[((int64_t)b * p.heads_kv + g) * p.nb + (cur.k0 >> 7)];
+      add[0] = qadd[0];
+      add[1] = qadd[1];
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[qb][r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const uint4 a = *(const uint4*)(buf + off256(32 * kb + lq, qk_chunk(s, lh)));
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) S[qb] = mma16<BF16>(a, qf[qb][s], S[qb]);
+      }
+      mul = p.scale_log2;
+      add[0] = 0.f;
+      add[1] = 0.f;
+    }
+
+    // ---- online softmax (log2 domain), one query per lane and query block
+    uint4 P[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float mx;
+      if (cur.partial) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = cur.k0 + 32 * kb + 8 * (r >> 2) + 4 * lh + (r & 3);
+          S[qb][r] = admit<MODE>(p, qinfo[qb], j) ? fmaf(S[qb][r], mul, add[qb]) : -INFINITY;
+        }
+        mx = S[qb][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[qb][r]);
+      } else {
+        float raw = S[qb][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) raw = fmaxf(raw, S[qb][r]);
+        mx = fmaf(raw, mul, add[qb]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m[qb], mx);
+      const bool resc = mnew > m[qb] + TAU;
+      const float alpha = resc ? exp2f(m[qb] - mnew) : 1.0f;
+      if (resc) m[qb] = mnew;
+      const float muse = (m[qb] == -INFINITY) ? 0.f : m[qb];
+      float ls = 0.f;
+      if (cur.partial) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          S[qb][r] = exp2f(S[qb][r] - muse);
+          ls += S[qb][r];
+        }
+      } else {
+        const float c = add[qb] - muse;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          S[qb][r] = exp2f(fmaf(S[qb][r], mul, c));
+          ls += S[qb][r];
+        }
+      }
+      l[qb] = l[qb] * alpha + ls;
+      if (__any(resc)) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) O[db][qb][r] *= alpha;
+      }
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const int r0 = 8 * k2;
+        P[qb][k2] = make_uint4(pack2<BF16>(S[qb][r0], S[qb][r0 + 1]), pack2<BF16>(S[qb][r0 + 2], S[qb][r0 + 3]),
+                               pack2<BF16>(S[qb][r0 + 4], S[qb][r0 + 5]),
+                               pack2<BF16>(S[qb][r0 + 6], S[qb][r0 + 7]));
+      }
+    }
+
+    // ---- O^T[d, q] += V^T[d, key] P^T[key, q] over these 32 keys (two k-steps of 16)
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const uint4 a = v_frag(buf + V_OFF, db, kb, k2, lane);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) O[db][qb] = mma16<BF16>(a, P[qb][k2], O[db][qb]);
+      }
+  }
+
+}
+
+template <bool BF16, int MODE>
+__global__ void __launch_bounds__(256) attn_fwd_kernel(const AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, lh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int qt, hg, b;
+  tile_coords((p.q_end - p.q_begin + QT - 1) / QT, p.heads_q / 4, &qt, &hg, &b);
+  const int h = hg * 4 + wave;
+  const int g = (hg * 4) / p.group;
+  const int q0 = p.q_begin + qt * QT;
+  const int qa = q0 >> 7;
+  {
+    // skip tiles holding no valid query (scanline text padding); uniform per workgroup
+    const int lo = q0, hi = min(q0 + QT, p.q_end);
+    const bool any = (MODE != kModeScan) ? lo < min(hi, p.n)
+                                         : (lo < min(hi, p.text)) || (max(lo, p.t_pad) < min(hi, p.t_pad + p.image));
+    if (!any) return;
+  }
+
+  uint4 qf[2][8];
+  load_q_frags<MODE>(p, b, h, q0 + lq, qf[0]);
+  load_q_frags<MODE>(p, b, h, q0 + 32 + lq, qf[1]);
+  const QInfo qinfo[2] = {query_info<MODE>(p, q0 + lq), query_info<MODE>(p, q0 + 32 + lq)};
+
+  // TileMix: INT8 codes of this query block, and the smooth_k row term.  Raw K is used on
+  // FP16 tiles and mean-centred codes on INT8 tiles; adding scale * q . mean to every INT8
+  // score puts both on the same per-row offset, which softmax ignores (smooth_k is exact
+  // for softmax, "The inputs that matter").
+  uint4 q8f[2][4];
+  float qadd[2] = {0.f, 0.f};
+  float sq_l2 = 0.f;
+  if (MODE == kModeTileMix && p.q_inv != nullptr) {
+    const int qidx = (b * p.heads_q + h) * p.nb + qa;
+    const float inv = p.q_inv[qidx];
+    sq_l2 = p.scale_log2 * p.q_scale[qidx];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) q8f[qb][s] = make_q8<BF16>(qf[qb][2 * s], qf[qb][2 * s + 1], inv);
+    if (p.smooth_k) {
+      const float* mean = p.k_mean + ((int64_t)b * p.heads_kv + g) * 128;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        float acc = 0.f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const uint4 x = qf[qb][s];
+          const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+          const float* mc = mean + 8 * qk_chunk(s, lh);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint16_t bits = (e & 1) ? (uint16_t)(w[e >> 1] >> 16) : (uint16_t)(w[e >> 1] & 0xffff);
+            acc = fmaf(elem_to_f32<BF16>(bits), mc[e], acc);
+          }
+        }
+        acc += __shfl_xor(acc, 32);
+        qadd[qb] = p.scale_log2 * acc;
+      }
+    }
+  }
+
+  int e0;
+  const int nsteps = step_count<MODE>(p, qa, &e0);
+  WaveState ws;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ws.O[db][qb][r] = 0.f;
+  ws.m[0] = ws.m[1] = -INFINITY;
+  ws.l[0] = ws.l[1] = 0.f;
+
+  if (nsteps > 0) {
+    StepInfo cur = step_info<MODE>(p, qa, e0, 0);
+    dma_stage<MODE>(p, b, g, cur, lds, wave, lane);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int i = 0; i < nsteps; ++i) {
+      const bool has_next = i + 1 < nsteps;
+      const StepInfo nxt = has_next ? step_info<MODE>(p, qa, e0, i + 1) : cur;
+      attn_step<BF16, MODE>(p, lds + (i & 1) * STAGE, lds + ((i + 1) & 1) * STAGE, cur, nxt, has_next, b, g, wave,
+                            lane, qf, q8f, qinfo, qadd, sq_l2, ws);
+      cur = nxt;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  }
+  const f32x16 (&O)[4][2] = ws.O;
+  const float (&l)[2] = ws.l;
+
+  // ---- epilogue: O = O^T / l, rows of valid queries only (padding is never written)
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float lt = l[qb] + __shfl_xor(l[qb], 32);
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    const int t = q0 + 32 * qb + lq;
+    if (!qinfo[qb].valid) continue;
+    uint16_t* dst = (uint16_t*)p.o + (int64_t)b * p.o_sb + (int64_t)tok_phys<MODE>(p, t) * p.o_st +
+                    (int64_t)h * p.o_sh;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        const f32x16& o = O[db][qb];
+        const uint2 val = make_uint2(pack2<BF16>(o[4 * grp] * inv, o[4 * grp + 1] * inv),
+                                     pack2<BF16>(o[4 * grp + 2] * inv, o[4 * grp + 3] * inv));
+        *(uint2*)(dst + 32 * db + 8 * grp + 4 * lh) = val;
+      }
+  }
+}
+// ---------------------------------------------------------------- quantiser
+// TileMix INT8 stage ("Krea 2 TileMix Attention (FP16/INT8 tiles)", "The inputs that
+// matter": smooth_k mean-centres K per head before quantisation).  Reproducible rule:
+// fp64 column sums of K, tokens of each 128-block added in order then the block sums in
+// order; m = fp32(sum / N); K_s = fp32(K) - m; per 128-token x 128-channel tile over
+// valid rows a = max |x|, inv = fp32(127 / a), scale = fp32(a / 127),
+// code = clamp(rint(x * inv), -127, 127).
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+// max over the 256 threads of the block (every thread gets the result)
+__device__ __forceinline__ float block_max256(float x, float* red) {
+  x = wave_max(x);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  const float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return r;
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(128) k_colsum_kernel(const QuantParams p) {
+  const int blk = blockIdx.x, g = blockIdx.y, b = blockIdx.z, c = threadIdx.x;
+  const uint16_t* src = (const uint16_t*)p.k.ptr + (int64_t)b * p.k.sb + (int64_t)g * p.k.sh + c;
+  const int t1 = min(p.n, blk * 128 + 128);
+  double acc = 0.0;
+  for (int t = blk * 128; t < t1; ++t) acc = __dadd_rn(acc, (double)elem_to_f32<BF16>(src[(int64_t)t * p.k.st]));
+  p.k_part[(((int64_t)b * p.heads_kv + g) * p.nb + blk) * 128 + c] = acc;
+}
+
+// Q tile scales: one workgroup per (batch, head, 128-token block).
+template <bool BF16>
+__global__ void __launch_bounds__(256) q_scale_kernel(const QuantParams p) {
+  __shared__ float red[4];
+  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const uint16_t* src = (const uint16_t*)p.q.ptr + (int64_t)b * p.q.sb + (int64_t)h * p.q.sh + (tid & 15) * 8;
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int t = blk * 128 + (tid >> 4) + 16 * i;
+    if (t < p.n) {
+      const uint4 x = *(const uint4*)(src + (int64_t)t * p.q.st);
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a = fmaxf(a, fabsf(elem_to_f32<BF16>(w[e] & 0xffff)));
+        a = fmaxf(a, fabsf(elem_to_f32<BF16>(w[e] >> 16)));
+      }
+    }
+  }
+  a = block_max256(a, red);
+  if (tid == 0) {
+    const int idx = ((int64_t)b * p.heads_q + h) * p.nb + blk;
+    p.q_inv[idx] = a > 0.f ? __fdiv_rn(127.0f, a) : 0.f;
+    p.q_scale[idx] = a > 0.f ? __fdiv_rn(a, 127.0f) : 0.f;
+  }
+}
+
+// K codes: one workgroup per (batch, KV head, 128-token block).  Each workgroup first
+// finishes the smooth_k mean from the fp64 block sums (same order everywhere).
+template <bool BF16>
+__global__ void __launch_bounds__(256) k_quant_kernel(const QuantParams p) {
+  __shared__ float mean[128];
+  __shared__ float red[4];
+  const int blk = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int64_t bg = (int64_t)b * p.heads_kv + g;
+  if (tid < 128) {
+    float m32 = 0.f;
+    if (p.smooth_k) {
+      double tot = 0.0;
+      for (int j = 0; j < p.nb; ++j) tot = __dadd_rn(tot, p.k_part[(bg * p.nb + j) * 128 + tid]);
+      m32 = __double2float_rn(__ddiv_rn(tot, (double)p.n));
+    }
+    mean[tid] = m32;
+    if (blk == 0) p.k_mean[bg * 128 + tid] = m32;
+  }
+  __syncthreads();
+  const int c8 = (tid & 15) * 8;
+  const uint16_t* src = (const uint16_t*)p.k.ptr + (int64_t)b * p.k.sb + (int64_t)g * p.k.sh + c8;
+  float x[8][8];
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int t = blk * 128 + (tid >> 4) + 16 * i;
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (t < p.n) raw = *(const uint4*)(src + (int64_t)t * p.k.st);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint16_t bits = (e & 1) ? (uint16_t)(w[e >> 1] >> 16) : (uint16_t)(w[e >> 1] & 0xffff);
+      x[i][e] = (t < p.n) ? __fsub_rn(elem_to_f32<BF16>(bits), mean[c8 + e]) : 0.f;
+      a = fmaxf(a, fabsf(x[i][e]));
+    }
+  }
+  a = block_max256(a, red);
+  const float inv = a > 0.f ? __fdiv_rn(127.0f, a) : 0.f;
+  if (tid == 0) p.k_scale[bg * p.nb + blk] = a > 0.f ? __fdiv_rn(a, 127.0f) : 0.f;
+  int8_t* dst = p.k_codes + ((bg * p.nb + blk) * 128) * 128 + c8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = (tid >> 4) + 16 * i;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      lo |= (uint32_t)(quant8(x[i][e], inv) & 255) << (8 * e);
+      hi |= (uint32_t)(quant8(x[i][e + 4], inv) & 255) << (8 * e);
+    }
+    *(uint2*)(dst + (int64_t)row * 128) = make_uint2(lo, hi);
+  }
+}
+
+// Q codes in natural layout [B, Hq, nb, 128, 128] with the attention kernel's quant8.
+template <bool BF16>
+__global__ void __launch_bounds__(256) q_codes_kernel(const QuantParams p, int8_t* out) {
+  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int64_t bh = (int64_t)b * p.heads_q + h;
+  const float inv = p.q_inv[bh * p.nb + blk];
+  const int c8 = (tid & 15) * 8;
+  const uint16_t* src = (const uint16_t*)p.q.ptr + (int64_t)b * p.q.sb + (int64_t)h * p.q.sh + c8;
+  int8_t* dst = out + ((bh * p.nb + blk) * 128) * 128 + c8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = (tid >> 4) + 16 * i, t = blk * 128 + row;
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (t < p.n) raw = *(const uint4*)(src + (int64_t)t * p.q.st);
+    *(uint2*)(dst + (int64_t)row * 128) =
+        make_uint2(quant4<BF16>(raw.x, raw.y, inv), quant4<BF16>(raw.z, raw.w, inv));
+  }
+}
+
+// ---------------------------------------------------------------- debug views
+// INT32 q8 . k8 of chosen 128x128 tiles through the attention kernel's INT8 path:
+// the same Q fragment load, in-register Q codes, INT8 K DMA staging and LDS layout,
+// and the same i8 MFMA fragment order.  One workgroup per tile; wave w owns query rows
+// 32 w .. 32 w + 31 of the tile.
+template <bool BF16>
+__global__ void __launch_bounds__(256) int8_scores_kernel(const AttnParams p, const int32_t* tiles, int32_t* out) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, lh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int* tl = tiles + 4 * blockIdx.x;
+  const int b = tl[0], h = tl[1], qa = tl[2], kb = tl[3];
+  const int g = h / p.group;
+  uint4 qf[8];
+  load_q_frags<kModeTileMix>(p, b, h, qa * 128 + 32 * wave + lq, qf);
+  const float inv = p.q_inv[((int64_t)b * p.heads_q + h) * p.nb + qa];
+  uint4 q8f[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) q8f[s] = make_q8<BF16>(qf[2 * s], qf[2 * s + 1], inv);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    StepInfo si;
+    si.k0 = kb * 128 + half * KT;
+    si.partial = false;
+    si.int8 = true;
+    dma_stage<kModeTileMix, false>(p, b, g, si, lds + half * STAGE, wave, lane);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int32_t* dst = out + (int64_t)blockIdx.x * 128 * 128;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const unsigned char* buf = lds + half * STAGE;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      i32x16 Si;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Si[r] = 0;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) Si = mma8(*(const uint4*)(buf + off128(32 * kb2 + lq, 2 * s + lh)), q8f[s], Si);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = half * KT + 32 * kb2 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        dst[(32 * wave + lq) * 128 + key] = Si[r];
+      }
+    }
+  }
+}
+
+// Keys admitted per logical query row, counted over the attention kernel's own step
+// list and element mask.
+template <int MODE>
+__global__ void __launch_bounds__(256) mask_counts_kernel(const AttnParams p, int32_t* out) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= p.length) return;
+  const QInfo qi = query_info<MODE>(p, t);
+  int count = 0;
+  if (qi.valid) {
+    const int qa = t >> 7;
+    int e0;
+    const int n = step_count<MODE>(p, qa, &e0);
+    for (int i = 0; i < n; ++i) {
+      const StepInfo s = step_info<MODE>(p, qa, e0, i);
+      if (!s.partial) {
+        count += KT;
+      } else {
+        for (int j = s.k0; j < s.k0 + KT; ++j) count += admit<MODE>(p, qi, j) ? 1 : 0;
+      }
+    }
+  }
+  out[t] = count;
+}
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_quant(const QuantParams& p, hipStream_t s) {
+  const dim3 gk(p.nb, p.heads_kv, p.batch), gq(p.nb, p.heads_q, p.batch);
+  if (p.bf16) {
+    if (p.smooth_k) hipLaunchKernelGGL(k_colsum_kernel<true>, gk, dim3(128), 0, s, p);
+    hipLaunchKernelGGL(q_scale_kernel<true>, gq, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(k_quant_kernel<true>, gk, dim3(256), 0, s, p);
+  } else {
+    if (p.smooth_k) hipLaunchKernelGGL(k_colsum_kernel<false>, gk, dim3(128), 0, s, p);
+    hipLaunchKernelGGL(q_scale_kernel<false>, gq, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(k_quant_kernel<false>, gk, dim3(256), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_q_codes(const QuantParams& p, int8_t* q_codes, hipStream_t s) {
+  const dim3 gq(p.nb, p.heads_q, p.batch);
+  if (p.bf16)
+    hipLaunchKernelGGL(q_codes_kernel<true>, gq, dim3(256), 0, s, p, q_codes);
+  else
+    hipLaunchKernelGGL(q_codes_kernel<false>, gq, dim3(256), 0, s, p, q_codes);
+  return hipGetLastError();
+}
+
+template <bool BF16, int MODE>
+static void launch_attn_t(const AttnParams& p, hipStream_t s) {
+  const int tiles = (p.q_end - p.q_begin + QT - 1) / QT * (p.heads_q / 4) * p.batch;
+  hipLaunchKernelGGL((attn_fwd_kernel<BF16, MODE>), dim3(tiles), dim3(256), 0, s, p);
+}
+
+hipError_t launch_attention(const AttnParams& p, int mode, bool bf16, hipStream_t s) {
+  if (bf16) {
+    if (mode == kModeDense) launch_attn_t<true, kModeDense>(p, s);
+    else if (mode == kModeTileMix) launch_attn_t<true, kModeTileMix>(p, s);
+    else launch_attn_t<true, kModeScan>(p, s);
+  } else {
+    if (mode == kModeDense) launch_attn_t<false, kModeDense>(p, s);
+    else if (mode == kModeTileMix) launch_attn_t<false, kModeTileMix>(p, s);
+    else launch_attn_t<false, kModeScan>(p, s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_int8_scores(const AttnParams& p, const int32_t* tiles, int n_tiles, int32_t* out, bool bf16,
+                              hipStream_t s) {
+  if (n_tiles <= 0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(int8_scores_kernel<true>, dim3(n_tiles), dim3(256), 0, s, p, tiles, out);
+  else
+    hipLaunchKernelGGL(int8_scores_kernel<false>, dim3(n_tiles), dim3(256), 0, s, p, tiles, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_counts(const AttnParams& p, int mode, int32_t* out, hipStream_t s) {
+  const dim3 grid((p.length + 255) / 256);
+  if (mode == kModeDense) hipLaunchKernelGGL(mask_counts_kernel<kModeDense>, grid, dim3(256), 0, s, p, out);
+  else if (mode == kModeTileMix) hipLaunchKernelGGL(mask_counts_kernel<kModeTileMix>, grid, dim3(256), 0, s, p, out);
+  else hipLaunchKernelGGL(mask_counts_kernel<kModeScan>, grid, dim3(256), 0, s, p, out);
+  return hipGetLastError();
+}
+
+}  // namespace krea

@@ -1,0 +1,65 @@
+// Kernel parameter blocks and launchers (device code lives in kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace krea {
+
+struct TensorRef {
+  const void* ptr;
+  int64_t sb, st, sh;  // element strides: batch, token, head (head_dim contiguous)
+};
+
+// Everything the attention kernel needs for one query slice.
+struct AttnParams {
+  TensorRef q, k, v;
+  void* o;
+  int64_t o_sb, o_st, o_sh;
+  int batch, heads_q, heads_kv, group;  // group = heads_q / heads_kv
+  int n;        // physical tokens
+  int text;     // T
+  int t_pad;    // logical start of image tokens
+  int image;    // image tokens
+  int cols;     // grid columns
+  uint32_t cols_magic;  // floor((2^32 - 1) / cols) for row division
+  int length;   // logical length
+  int nb;       // 128-token blocks per side
+  int q_begin, q_end;  // logical query range of this launch
+  float scale_log2;    // softmax_scale * log2(e)
+  int half_window;     // window / 2 (scanline)
+  int tile_aligned;
+  int smooth_k;
+  const uint8_t* route;    // TileMix [nb * nb]
+  const int32_t* row_ptr;  // scanline tile lists
+  const int32_t* cols_list;
+  const float* k_mean;     // [B, Hkv, 128]
+  const int8_t* k_codes;   // [B, Hkv, nb, 128, 128]
+  const float* k_scale;    // [B, Hkv, nb]
+  const float* q_inv;      // [B, Hq, nb]
+  const float* q_scale;    // [B, Hq, nb]
+};
+
+// Quantiser stage for TileMix (smooth_k mean, K codes, Q scales).
+struct QuantParams {
+  TensorRef q, k;
+  int batch, heads_q, heads_kv, n, text, nb;
+  int smooth_k;
+  int bf16;           // element type of q and k: 1 bf16, 0 fp16
+  double* k_part;     // [B, Hkv, nb, 128] fp64 block column sums
+  float* k_mean;      // [B, Hkv, 128]
+  int8_t* k_codes;    // [B, Hkv, nb, 128, 128]
+  float* k_scale;     // [B, Hkv, nb]
+  float* q_inv;       // [B, Hq, nb]
+  float* q_scale;     // [B, Hq, nb]
+};
+
+hipError_t launch_quant(const QuantParams& p, hipStream_t s);
+hipError_t launch_attention(const AttnParams& p, int mode, bool bf16, hipStream_t s);
+hipError_t launch_q_codes(const QuantParams& p, int8_t* q_codes, hipStream_t s);
+hipError_t launch_int8_scores(const AttnParams& p, const int32_t* tiles, int n_tiles, int32_t* out,
+                              bool bf16, hipStream_t s);
+hipError_t launch_mask_counts(const AttnParams& p, int mode, int32_t* out, hipStream_t s);
+
+}  // namespace krea

@@ -1,0 +1,62 @@
+// Host planner: argument validation, logical token layout, TileMix route map,
+// scanline block mask and per-query-block tile lists, workspace layout.
+// Pure C++ (no HIP), so every rule here is testable without a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "krea_attn.h"
+
+namespace krea {
+
+constexpr int kTile = 128;     // route / mask granularity (tokens)
+constexpr int kHeadDim = 128;  // the only supported head size
+
+// Logical sequence.  Dense and TileMix use the unpadded sequence (t_pad == text,
+// length == N).  Scanline pads text and the image tail to multiples of 128
+// ("Krea 2 Scanline Attention", "What the mask actually is").
+struct Layout {
+  int text = 0;       // T
+  int t_pad = 0;      // logical start of the image tokens
+  int image = 0;      // I = rows * cols
+  int cols = 1;       // grid columns (scanline rows = (t - t_pad) / cols)
+  int n = 0;          // physical tokens N = T + I
+  int length = 0;     // logical length (N, or padded to a multiple of 128)
+  int nb = 0;         // 128-token blocks per side
+};
+
+struct Plan {
+  Layout lay;
+  int mode = ATTN_DENSE;
+  std::vector<uint8_t> route;    // TileMix [nb * nb], 1 = INT8
+  std::vector<uint8_t> bmask;    // scanline [nb * nb], 0 skip / 1 full / 2 partial
+  // Per query block tile list (scanline): entries of block a are
+  // cols[row_ptr[a] .. row_ptr[a + 1]), each (key block) | (partial << 16).
+  std::vector<int32_t> row_ptr;
+  std::vector<int32_t> cols;
+  int64_t int8_tiles = 0, active_tiles = 0, partial_tiles = 0;
+};
+
+// Offsets of the TileMix workspace regions (bytes, 256-aligned).
+struct WorkspaceLayout {
+  size_t k_part = 0, k_mean = 0, k_codes = 0, k_scale = 0, q_inv = 0, q_scale = 0;
+  size_t total = 0;
+};
+
+// Returns ATTN_OK or an error code with `err` set.
+attn_status validate_args(const attn_args& a, std::string& err);
+Layout make_layout(const attn_args& a);
+WorkspaceLayout workspace_layout(const attn_args& a);
+
+uint64_t splitmix64(uint64_t x);
+std::vector<uint8_t> build_route_map(const attn_args& a, const Layout& lay, int64_t* n_int8);
+std::vector<uint8_t> build_block_mask(const attn_args& a, const Layout& lay);
+Plan build_plan(const attn_args& a);
+
+// Key identifying everything a plan depends on (for the plan cache).
+std::string plan_key(const attn_args& a);
+
+}  // namespace krea

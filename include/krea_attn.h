@@ -1,0 +1,163 @@
+/*
+ * krea_attn.h -- C ABI of the MI355X (gfx950) joint [text, image] attention library.
+ *
+ * The operation is the bidirectional softmax attention inside each single-stream
+ * block of Krea 2 ("Krea 2 TileMix Attention (FP16/INT8 tiles)", section "What it
+ * actually patches": attn(q, k, v) over the joint [text, image] sequence, 48 query
+ * heads over 12 KV heads resolved in the kernel instead of by repeat_interleave):
+ *
+ *   O[b, i, h, :] = sum_j softmax_j(s_ij) V[b, j, h / (Hq/Hkv), :]
+ *
+ * in one of three modes:
+ *   ATTN_DENSE    every key, s_ij = scale * q_i . k_j (FP16/BF16 MFMA, fp32 softmax);
+ *   ATTN_TILEMIX  each 128x128 tile of the score matrix goes to an FP16 or an INT8
+ *                 path by a static map (text tiles and a diagonal band stay FP16,
+ *                 a percentage of the other image-image tiles go INT8, K mean-centred
+ *                 by smooth_k); both paths feed one running softmax -- same page,
+ *                 sections "What it actually patches" and "The inputs that matter";
+ *   ATTN_SCANLINE text is global, an image token sees image tokens within
+ *                 window / 2 grid rows of its own, text and image tail padded to
+ *                 128-token tiles, block mask at 128 tiles ("Krea 2 Scanline
+ *                 Attention", sections "What the mask actually is" and "The settings
+ *                 that matter").
+ * Any mode may run its queries in slices of q_chunk tokens, each slice against the
+ * full K/V ("LayerStream: Krea2 Chunking", section "What the node does to the
+ * block", attn_chunk_tokens); the result does not depend on the slicing.
+ *
+ * Conventions for every entry point:
+ *   - Tensors are described by attn_tensor: a device pointer and element strides for
+ *     batch, token and head; head_dim is contiguous.  q is [B, N, Hq, 128], k and v
+ *     are [B, N, Hkv, 128], o is [B, N, Hq, 128], N = text_tokens + img_rows*img_cols,
+ *     tokens text first then the image grid row by row.  Pointers must be 16-byte
+ *     aligned and strides multiples of 8 elements.
+ *   - The caller owns q, k, v, o, the workspace and the stream.  Device entry points
+ *     only enqueue work on the given HIP stream (NULL = the null stream) and return
+ *     without synchronising.  The library owns a cache of at most 8 plans (route
+ *     maps, block masks, tile lists) with their device copies, keyed by device and
+ *     every shape and mode argument; a cache miss builds the plan on the host and
+ *     copies it to the device synchronously before enqueueing.
+ *   - Every argument is validated before any device work.  Errors are returned as
+ *     attn_status codes, never thrown; attn_last_error() gives a message for the
+ *     calling thread.  There is no fallback path: an unsupported input is an error.
+ */
+#ifndef KREA_ATTN_H
+#define KREA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t attn_status;
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = -1,      /* null pointer, bad enum, bad percentage/window/q_chunk, misalignment */
+  ATTN_ERR_UNSUPPORTED_DTYPE = -2, /* fp32 inputs are refused (the TileMix page lists fp32 as a reason the
+                                      fused kernel does not run, "Where people get burned") */
+  ATTN_ERR_SHAPE = -3,            /* head_dim != 128, Hq % Hkv, (Hq/Hkv) % 4, sizes <= 0 or too large */
+  ATTN_ERR_WORKSPACE = -4,        /* workspace smaller than attn_workspace_bytes() */
+  ATTN_ERR_DEVICE = -5            /* a HIP runtime call failed */
+};
+
+enum { ATTN_F16 = 0, ATTN_BF16 = 1, ATTN_F32 = 2 };
+enum { ATTN_DENSE = 0, ATTN_TILEMIX = 1, ATTN_SCANLINE = 2 };
+enum { ATTN_PAT_ZERO = 0, ATTN_PAT_ONE = 1, ATTN_PAT_BAND = 2 };
+
+typedef struct {
+  void* ptr;        /* device pointer to element [0, 0, 0, 0] */
+  int64_t stride_b; /* elements between batches */
+  int64_t stride_t; /* elements between tokens */
+  int64_t stride_h; /* elements between heads */
+} attn_tensor;
+
+typedef struct {
+  int32_t batch;        /* B >= 1 */
+  int32_t heads_q;      /* Hq; Hq % Hkv == 0 and (Hq / Hkv) % 4 == 0 */
+  int32_t heads_kv;     /* Hkv */
+  int32_t head_dim;     /* must be 128 (Krea 2: hidden 6144 / 48 heads) */
+  int32_t text_tokens;  /* T >= 0, text first in the joint sequence */
+  int32_t img_rows;     /* image token grid rows (scanline uses the rows) */
+  int32_t img_cols;     /* image token grid columns; N = T + rows * cols >= 1 */
+  int32_t dtype;        /* ATTN_BF16 or ATTN_F16 (ATTN_F32 -> ATTN_ERR_UNSUPPORTED_DTYPE) */
+  float softmax_scale;  /* applied to q.k; 0 means 1/sqrt(head_dim) rounded to fp32 */
+  int32_t mode;         /* ATTN_DENSE / ATTN_TILEMIX / ATTN_SCANLINE */
+  /* TileMix ("Krea 2 TileMix Attention", "The inputs that matter") */
+  int32_t pattern;      /* ATTN_PAT_ZERO (all FP16), ATTN_PAT_ONE (every image-image tile INT8),
+                           ATTN_PAT_BAND (diagonal band FP16, percentage of the rest INT8) */
+  double percentage;    /* in [0, 1]: share of the image-image tiles outside the band sent to INT8;
+                           count = floor(percentage * candidates) */
+  int32_t band_blocks;  /* band half-width w >= 0 in 128-token blocks: |a - b| <= w stays FP16 */
+  int32_t smooth_k;     /* nonzero: subtract the per-(batch, KV head, channel) mean of K before INT8 */
+  uint64_t seed;        /* seeded pick of INT8 tiles: smallest SplitMix64(seed ^ (a << 32 | b)) */
+  /* Scanline ("Krea 2 Scanline Attention", "The settings that matter") */
+  int32_t window;       /* odd, 1..255; image tokens see rows within window / 2 */
+  int32_t tile_aligned; /* nonzero: admit every valid pair inside an active 128x128 tile */
+  /* Query slicing ("LayerStream: Krea2 Chunking", attn_chunk_tokens) */
+  int32_t q_chunk;      /* 0 = one pass; else a multiple of 128 query positions per slice */
+  int32_t reserved;     /* must be 0 */
+} attn_args;
+
+typedef struct {
+  int32_t n_blocks;       /* 128-token blocks per side of the (logical) score matrix */
+  int32_t text_blocks;    /* blocks holding a text token */
+  int32_t logical_tokens; /* N, or the padded length for scanline */
+  int32_t text_pad;       /* text length after padding (scanline), else text_tokens */
+  int64_t int8_tiles;     /* TileMix: tiles routed to INT8 */
+  int64_t active_tiles;   /* tiles the kernel visits (nb*nb for dense/TileMix) */
+  int64_t partial_tiles;  /* visited tiles that need element masking */
+} attn_plan_info;
+
+/* Bytes of device workspace attn_forward needs for these arguments (0 for dense and
+ * scanline; TileMix holds the smooth_k partial sums and mean, INT8 K codes and scales,
+ * and Q scales).  Host only. */
+attn_status attn_workspace_bytes(const attn_args* args, size_t* bytes);
+
+/* The attention call.  q, k, v are read, o is written (rows of every valid token;
+ * padding never appears in o).  workspace: device memory of at least
+ * attn_workspace_bytes() bytes (may be NULL when that is 0); its contents on entry
+ * do not matter and are overwritten.  Enqueued on `stream` (a hipStream_t). */
+attn_status attn_forward(const attn_args* args, const attn_tensor* q, const attn_tensor* k,
+                         const attn_tensor* v, const attn_tensor* o, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Host-only plan exports (no GPU needed). */
+attn_status attn_plan_info_get(const attn_args* args, attn_plan_info* out);
+/* TileMix route map, row-major uint8 [nb][nb] over (query block, key block): 0 FP16, 1 INT8. */
+attn_status attn_route_map(const attn_args* args, uint8_t* out, int32_t nb);
+/* Scanline block mask, row-major uint8 [nb][nb] over logical tiles: 0 skip, 1 full, 2 partial. */
+attn_status attn_block_mask(const attn_args* args, uint8_t* out, int32_t nb);
+
+/* Device debug exports.  They run the same device functions as attn_forward.
+ *
+ * attn_quantize: the smooth_k mean and per-tile INT8 stage of TileMix ("The inputs that
+ * matter", smooth_k).  Writes (each output may be NULL) k_mean float [B, Hkv, 128],
+ * k_codes int8 [B, Hkv, nb, 128, 128], k_scale float [B, Hkv, nb], q_codes int8
+ * [B, Hq, nb, 128, 128], q_scale float [B, Hq, nb]; code rows past N are zero.  Codes are
+ * written for every block that is not a text block. */
+attn_status attn_quantize(const attn_args* args, const attn_tensor* q, const attn_tensor* k,
+                          void* workspace, size_t workspace_bytes, float* k_mean,
+                          int8_t* k_codes, float* k_scale, int8_t* q_codes, float* q_scale,
+                          void* stream);
+
+/* attn_int8_scores: INT32 accumulators q8 . k8 of chosen 128x128 tiles, through the INT8
+ * MFMA path of the attention kernel.  tiles: device int32 [n_tiles][4] = (b, h, a, kb);
+ * out: device int32 [n_tiles][128 query rows][128 keys].  Runs the quantiser first. */
+attn_status attn_int8_scores(const attn_args* args, const attn_tensor* q, const attn_tensor* k,
+                             void* workspace, size_t workspace_bytes, const int32_t* tiles,
+                             int32_t n_tiles, int32_t* out, void* stream);
+
+/* attn_mask_row_counts: number of keys each logical query row admits, evaluated by the
+ * kernel's own tile list and element mask.  out: device int32 [logical_tokens]. */
+attn_status attn_mask_row_counts(const attn_args* args, int32_t* out, void* stream);
+
+const char* attn_status_string(attn_status status);
+/* Message for the last error on the calling thread ("" if none). */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KREA_ATTN_H */

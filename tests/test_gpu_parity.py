@@ -1,0 +1,243 @@
+"""HIP path vs the fp64 CPU oracle, through the C ABI, on an MI355X.
+
+Tolerance for outputs (unit-variance inputs): max |err| <= 2e-2 and mean |err| <= 2e-3
+against the fp64 oracle, plus relative RMS <= 1e-2 as an internal gate.  Route maps,
+masks, INT8 codes, scales and INT32 accumulators are compared bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import diffusion_transformer_attention_bidirectional_amd as ka
+from oracle import attn_ref, plan_ref, quant_ref
+from synth import WORKLOADS, Workload, make_qkv, to_f64
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, MEAN_ABS, REL_RMS = 2e-2, 2e-3, 1e-2
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ka.load_library()
+    return torch.device("cuda:0")
+
+
+def _w(**kw):
+    base = dict(name="case", batch=1, heads_q=8, heads_kv=2, head_dim=128, text_tokens=40, img_rows=10,
+                img_cols=26, dtype="bf16", seed=7, offset_std=0.5, mode="dense")
+    base.update(kw)
+    return Workload(**base)
+
+
+def _kw(w):
+    return dict(text_tokens=w.text_tokens, img_rows=w.img_rows, img_cols=w.img_cols, mode=w.mode,
+                pattern=w.pattern, percentage=w.percentage, band_blocks=w.band_blocks, seed=w.route_seed,
+                smooth_k=w.smooth_k, window=w.window, tile_aligned=w.tile_aligned, q_chunk=w.q_chunk,
+                softmax_scale=w.softmax_scale)
+
+
+def _run(w, dev, q=None, k=None, v=None, **over):
+    if q is None:
+        q, k, v = make_qkv(w)
+    kw = _kw(w)
+    kw.update(over)
+    out = ka.attention(q.to(dev), k.to(dev), v.to(dev), **kw)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), (q, k, v)
+
+
+def _assert_close(got, ref, what=""):
+    err = np.abs(got - ref)
+    rel = np.sqrt(np.mean((got - ref) ** 2) / max(np.mean(ref ** 2), 1e-30))
+    assert np.isfinite(got).all(), what
+    assert err.max() <= MAX_ABS, f"{what}: max abs {err.max():.3e}"
+    assert err.mean() <= MEAN_ABS, f"{what}: mean abs {err.mean():.3e}"
+    assert rel <= REL_RMS, f"{what}: rel rms {rel:.3e}"
+    return err.max(), err.mean(), rel
+
+
+# ----------------------------------------------------------------------------- small, full oracle
+SMALL = [
+    ("tiny_f16", WORKLOADS["tiny"]),
+    ("dense_bf16_ragged", _w()),
+    ("dense_f16_ragged", _w(dtype="f16")),
+    ("dense_b2_g8", _w(batch=2, heads_q=8, heads_kv=1, text_tokens=64, img_rows=9, img_cols=21)),
+    ("tilemix_band", _w(mode="tilemix", pattern="band", percentage=0.6, band_blocks=1, smooth_k=True,
+                        text_tokens=130, img_rows=12, img_cols=40)),
+    ("tilemix_band_f16", _w(dtype="f16", mode="tilemix", pattern="band", percentage=0.5, band_blocks=0,
+                            smooth_k=True, text_tokens=130, img_rows=12, img_cols=40)),
+    ("tilemix_one_nosmooth", _w(mode="tilemix", pattern="one", smooth_k=False, text_tokens=100, img_rows=8,
+                                img_cols=50)),
+    ("tilemix_zero_smooth", _w(mode="tilemix", pattern="zero", smooth_k=True)),
+    ("scan_aligned", _w(mode="scanline", window=3, tile_aligned=True, text_tokens=77)),
+    ("scan_exact", _w(mode="scanline", window=3, tile_aligned=False, text_tokens=77)),
+    ("scan_w1_exact", _w(mode="scanline", window=1, tile_aligned=False, text_tokens=130, img_rows=12,
+                         img_cols=40)),
+    ("scan_textpad_tail", _w(mode="scanline", window=5, tile_aligned=True, text_tokens=200, img_rows=7,
+                             img_cols=33)),
+]
+
+
+@pytest.mark.parametrize("name,w", SMALL, ids=[n for n, _ in SMALL])
+def test_small_vs_oracle(dev, name, w):
+    got, (q, k, v) = _run(w, dev)
+    ref = attn_ref.attention(to_f64(q), to_f64(k), to_f64(v), w)
+    mx, mn, rel = _assert_close(got, ref, name)
+    print(f"{name}: max {mx:.2e} mean {mn:.2e} rel {rel:.2e}")
+
+
+@pytest.mark.parametrize("w", [
+    _w(),
+    _w(mode="tilemix", pattern="band", percentage=0.6, band_blocks=1, smooth_k=True, text_tokens=130,
+       img_rows=12, img_cols=40),
+    _w(mode="scanline", window=3, tile_aligned=False, text_tokens=77),
+], ids=["dense", "tilemix", "scanline"])
+def test_slices_bit_identical(dev, w):
+    full, qkv = _run(w, dev)
+    for chunk in (128, 256):
+        sliced, _ = _run(w, dev, *qkv, q_chunk=chunk)
+        assert (sliced == full).all()
+
+
+def test_zero_pattern_bit_identical_to_dense(dev):
+    w = _w(offset_std=0.5)
+    dense, qkv = _run(w, dev)
+    for smooth in (False, True):
+        z, _ = _run(w, dev, *qkv, mode="tilemix", pattern="zero", smooth_k=smooth)
+        assert (z == dense).all()
+
+
+def test_deterministic(dev):
+    w = _w(mode="tilemix", pattern="band", percentage=0.5, band_blocks=1, smooth_k=True, text_tokens=130,
+           img_rows=12, img_cols=40)
+    a, qkv = _run(w, dev)
+    b, _ = _run(w, dev, *qkv)
+    assert (a == b).all()
+
+
+@pytest.mark.parametrize("t,rows,cols", [(1, 0, 0), (5, 0, 0), (0, 1, 1), (129, 0, 0), (0, 3, 43), (7, 11, 13)])
+def test_edge_sizes_dense(dev, t, rows, cols):
+    w = _w(heads_q=4, heads_kv=1, text_tokens=t, img_rows=rows, img_cols=cols)
+    got, (q, k, v) = _run(w, dev)
+    ref = attn_ref.attention(to_f64(q), to_f64(k), to_f64(v), w)
+    _assert_close(got, ref, f"N={w.tokens}")
+
+
+def test_edge_scanline_pure_image_and_tiny_grid(dev):
+    for w in (_w(mode="scanline", window=1, tile_aligned=False, text_tokens=0, img_rows=9, img_cols=30),
+              _w(mode="scanline", window=255, tile_aligned=True, text_tokens=3, img_rows=2, img_cols=2)):
+        got, (q, k, v) = _run(w, dev)
+        ref = attn_ref.attention(to_f64(q), to_f64(k), to_f64(v), w)
+        _assert_close(got, ref, f"scan {w.text_tokens}+{w.img_rows}x{w.img_cols}")
+
+
+def test_strided_bhnd_layout(dev):
+    # [B, H, N, d] storage viewed as [B, N, H, d]: strides are passed through the ABI
+    w = _w(batch=2)
+    q, k, v = make_qkv(w)
+    qs = q.permute(0, 2, 1, 3).contiguous().to(dev).permute(0, 2, 1, 3)
+    ks = k.permute(0, 2, 1, 3).contiguous().to(dev).permute(0, 2, 1, 3)
+    vs = v.permute(0, 2, 1, 3).contiguous().to(dev).permute(0, 2, 1, 3)
+    out = torch.empty(q.shape[0], q.shape[2], q.shape[1], 128, dtype=q.dtype, device=dev).permute(0, 2, 1, 3)
+    ka.attention(qs, ks, vs, out=out, **_kw(w))
+    torch.cuda.synchronize()
+    ref = attn_ref.attention(to_f64(q), to_f64(k), to_f64(v), w)
+    _assert_close(out.float().cpu().numpy().astype(np.float64), ref, "strided")
+
+
+# ----------------------------------------------------------------------------- bit-exact pieces
+def _quant_check(w, dev):
+    q, k, v = make_qkv(w)
+    args = ka.args_for(q, k, **{kk: vv for kk, vv in _kw(w).items()})
+    res = ka.quantize(q.to(dev), k.to(dev), args)
+    torch.cuda.synchronize()
+    qf, kf = to_f64(q), to_f64(k)
+    m32 = quant_ref.k_mean(kf) if w.smooth_k else np.zeros((w.batch, w.heads_kv, 128), np.float32)
+    k8, sk, _ = quant_ref.quantize_tiles(quant_ref.smooth(kf, m32 if w.smooth_k else None))
+    q8, sq, _ = quant_ref.quantize_tiles(qf.astype(np.float32))
+    if w.smooth_k:
+        assert (res["k_mean"].cpu().numpy().view(np.uint32) == m32.view(np.uint32)).all()
+    assert (res["k_scale"].cpu().numpy().view(np.uint32) == sk.view(np.uint32)).all()
+    assert (res["q_scale"].cpu().numpy().view(np.uint32) == sq.view(np.uint32)).all()
+    assert (res["k_codes"].cpu().numpy() == k8).all()
+    assert (res["q_codes"].cpu().numpy() == q8).all()
+    return q, k, args, q8, k8
+
+
+def test_quantiser_bit_exact_small(dev):
+    _quant_check(_w(mode="tilemix", smooth_k=True, text_tokens=130, img_rows=12, img_cols=40), dev)
+    _quant_check(_w(mode="tilemix", smooth_k=False, dtype="f16", text_tokens=10, img_rows=3, img_cols=50), dev)
+
+
+def test_int8_scores_bit_exact(dev):
+    w = _w(mode="tilemix", smooth_k=True, text_tokens=130, img_rows=12, img_cols=40)
+    q, k, args, q8, k8 = _quant_check(w, dev)
+    nb = q8.shape[2]
+    tiles = [(0, h, a, b) for h in (0, 3, 7) for a in range(nb) for b in (0, nb - 1, 2)]
+    got = ka.int8_scores(q.to(dev), k.to(dev), args, tiles).cpu().numpy()
+    for i, (b, h, a, kb) in enumerate(tiles):
+        want = quant_ref.int_scores(q8[b, h, a], k8[b, h // 4, kb])
+        assert (got[i] == want).all(), (b, h, a, kb)
+
+
+@pytest.mark.parametrize("t,rows,cols,window,aligned", [
+    (512, 64, 64, 11, True), (512, 64, 64, 11, False), (77, 10, 26, 3, True), (77, 10, 26, 3, False),
+    (0, 9, 30, 1, False), (200, 7, 33, 5, True)])
+def test_mask_row_counts_bit_exact(dev, t, rows, cols, window, aligned):
+    args = ka.make_args(text_tokens=t, img_rows=rows, img_cols=cols, mode="scanline", window=window,
+                        tile_aligned=aligned)
+    got = ka.mask_row_counts(args, device=dev).cpu().numpy()
+    lay = plan_ref.ScanLayout(t, rows, cols)
+    bm = plan_ref.block_mask(t, rows, cols, window, aligned)
+    want = np.zeros(lay.length, np.int64)
+    for a in range(lay.length // 128):
+        r = np.arange(a * 128, a * 128 + 128)
+        want[r] = plan_ref.admitted(lay, window, aligned, r, bm).sum(axis=1)
+    assert (got == want).all()
+
+
+def test_mask_row_counts_dense_and_tilemix(dev):
+    for mode in ("dense", "tilemix"):
+        args = ka.make_args(text_tokens=40, img_rows=10, img_cols=26, mode=mode)
+        got = ka.mask_row_counts(args, device=dev).cpu().numpy()
+        assert (got == 300).all()
+
+
+# ----------------------------------------------------------------------------- full Krea shapes
+def _sample_rows(n, t, rng, count=48):
+    rows = set([0, t - 1, t, t + 1, n - 1, n // 2, 127, 128]) | set(rng.integers(0, n, count).tolist())
+    return np.array(sorted(r for r in rows if 0 <= r < n))
+
+
+@pytest.mark.parametrize("name", ["1mp_dense", "1mp_band", "1mp_scanline", "4mp_band"])
+def test_krea_shapes_sampled(dev, name):
+    w = WORKLOADS[name]
+    got, (q, k, v) = _run(w, dev)
+    ora = attn_ref.Oracle(to_f64(q), to_f64(k), to_f64(v), w)
+    rng = np.random.default_rng(3)
+    rows = _sample_rows(w.tokens, w.text_tokens, rng)
+    errs = []
+    for h in (0, 5, 22, 47):
+        ref = ora.rows(0, h, rows)
+        mx, mn, rel = _assert_close(got[0, rows, h], ref, f"{name} head {h}")
+        errs.append((mx, mn, rel))
+    print(name, "max/mean/rel per head:", [(f"{a:.1e}", f"{b:.1e}", f"{c:.1e}") for a, b, c in errs])
+    assert np.isfinite(got).all()
+
+
+def test_krea_1mp_quantiser_bit_exact(dev):
+    _quant_check(WORKLOADS["1mp_band"], dev)
+
+
+def test_krea_1mp_scanline_counts(dev):
+    w = WORKLOADS["1mp_scanline"]
+    args = ka.make_args(text_tokens=512, img_rows=64, img_cols=64, mode="scanline", window=11, tile_aligned=True)
+    got = ka.mask_row_counts(args, device=dev).cpu().numpy()
+    assert int(got.sum()) == 7_929_856
+    args0 = ka.make_args(text_tokens=512, img_rows=64, img_cols=64, mode="scanline", window=11,
+                         tile_aligned=False)
+    assert int(ka.mask_row_counts(args0, device=dev).cpu().numpy().sum()) == 7_217_152
+    del w

@@ -1,0 +1,215 @@
+"""C-ABI library on the CPU: symbols, host planner vs oracle (bit-exact), validation.
+
+No compute call reaches a GPU here: only host exports, and attn_forward calls that
+fail validation before any device work.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import diffusion_transformer_attention_bidirectional_amd as ka
+from oracle import plan_ref
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ka.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return ka.load_library()
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "krea_attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert set(names) == set(ka.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_layout_matches_header(tmp_path):
+    # compile a probe against the header and compare every offset with the ctypes mirror
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "krea_attn.h"', "int main(void) {"]
+    for struct, cls in (("attn_args", ka.AttnArgs), ("attn_tensor", ka.AttnTensor),
+                        ("attn_plan_info", ka.AttnPlanInfo)):
+        lines.append(f'printf("{struct} %zu\\n", sizeof({struct}));')
+        for f, _ in cls._fields_:
+            lines.append(f'printf("{struct}.{f} %zu\\n", offsetof({struct}, {f}));')
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                  check=True).stdout.splitlines())
+    for struct, cls in (("attn_args", ka.AttnArgs), ("attn_tensor", ka.AttnTensor),
+                        ("attn_plan_info", ka.AttnPlanInfo)):
+        assert int(got[struct]) == ctypes.sizeof(cls)
+        for f, _ in cls._fields_:
+            assert int(got[f"{struct}.{f}"]) == getattr(cls, f).offset, (struct, f)
+
+
+ROUTE_CASES = [
+    (4608, 512, "band", 0.5, 2, 0),
+    (16896, 512, "band", 0.75, 2, 0),
+    (1500, 200, "band", 0.37, 1, 12345),
+    (1500, 200, "one", 0.3, 1, 7),
+    (1500, 200, "zero", 0.5, 2, 0),
+    (300, 0, "band", 0.9, 0, 2**63 + 5),
+    (129, 1, "band", 1.0, 0, 3),
+    (5000, 77, "band", 0.2, 3, 99),
+]
+
+
+@pytest.mark.parametrize("n,t,pattern,pct,w,seed", ROUTE_CASES)
+def test_route_map_bit_exact_vs_oracle(lib, n, t, pattern, pct, w, seed):
+    args = ka.make_args(text_tokens=t, img_rows=1, img_cols=n - t, mode="tilemix", pattern=pattern,
+                        percentage=pct, band_blocks=w, seed=seed)
+    got = ka.route_map(args)
+    want = plan_ref.route_map(n, t, pattern, pct, w, seed)
+    assert got.shape == want.shape and (got == want).all()
+    assert ka.plan_info(args)["int8_tiles"] == int(want.sum())
+
+
+MASK_CASES = [
+    (512, 64, 64, 11, True), (512, 64, 64, 11, False), (77, 10, 12, 3, True), (77, 10, 12, 3, False),
+    (5, 7, 9, 1, False), (130, 6, 40, 5, True), (0, 20, 20, 1, False), (300, 1, 50, 255, False),
+    (64, 8, 8, 1, True), (512, 30, 17, 7, False),
+]
+
+
+@pytest.mark.parametrize("t,rows,cols,window,aligned", MASK_CASES)
+def test_block_mask_bit_exact_vs_oracle(lib, t, rows, cols, window, aligned):
+    args = ka.make_args(text_tokens=t, img_rows=rows, img_cols=cols, mode="scanline", window=window,
+                        tile_aligned=aligned)
+    got = ka.block_mask(args)
+    want = plan_ref.block_mask(t, rows, cols, window, aligned)
+    assert (got == want).all()
+    info = ka.plan_info(args)
+    assert info["active_tiles"] == int((want != 0).sum())
+    assert info["partial_tiles"] == int((want == 2).sum())
+    assert info["logical_tokens"] == plan_ref.ScanLayout(t, rows, cols).length
+
+
+@pytest.mark.slow
+def test_block_mask_4mp_vs_oracle(lib):
+    args = ka.make_args(text_tokens=512, img_rows=128, img_cols=128, mode="scanline", window=11)
+    assert (ka.block_mask(args) == plan_ref.block_mask(512, 128, 128, 11, True)).all()
+
+
+def test_workspace_sizes(lib):
+    assert ka.workspace_bytes(ka.make_args(text_tokens=512, img_rows=64, img_cols=64)) == 0
+    scan = ka.make_args(text_tokens=512, img_rows=64, img_cols=64, mode="scanline")
+    assert ka.workspace_bytes(scan) == 0
+    tm = ka.make_args(text_tokens=512, img_rows=64, img_cols=64, mode="tilemix")
+    n = ka.workspace_bytes(tm)
+    # at least the INT8 K codes: 12 KV heads x 36 blocks x 128 x 128
+    assert n >= 12 * 36 * 128 * 128
+
+
+def _status(fn, *a):
+    return fn(*a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype="f32"), -2),
+    (dict(head_dim=64), -3),
+    (dict(heads_q=48, heads_kv=7), -3),
+    (dict(heads_q=12, heads_kv=6), -3),
+    (dict(batch=0), -3),
+    (dict(text_tokens=0, img_rows=0, img_cols=0), -3),
+    (dict(mode=7), -1),
+    (dict(q_chunk=100), -1),
+    (dict(q_chunk=-128), -1),
+    (dict(mode="tilemix", percentage=1.5), -1),
+    (dict(mode="tilemix", percentage=-0.1), -1),
+    (dict(mode="tilemix", pattern=9), -1),
+    (dict(mode="tilemix", band_blocks=-1), -1),
+    (dict(mode="scanline", window=10), -1),
+    (dict(mode="scanline", window=257), -1),
+    (dict(mode="scanline", window=0), -1),
+    (dict(softmax_scale=-1.0), -1),
+])
+def test_validation_codes(lib, kw, status):
+    base = dict(text_tokens=512, img_rows=64, img_cols=64)
+    base.update(kw)
+    args = ka.make_args(**base)
+    n = ctypes.c_size_t(0)
+    assert lib.attn_workspace_bytes(ctypes.byref(args), ctypes.byref(n)) == status
+    assert lib.attn_last_error()  # a message is set
+    info = ka.AttnPlanInfo()
+    assert lib.attn_plan_info_get(ctypes.byref(args), ctypes.byref(info)) == status
+
+
+def _fake(h):
+    # aligned, non-null fake device pointers: validation must fail before any use
+    return ka.AttnTensor(0x100000, 4608 * h * 128, h * 128, 128)
+
+
+def test_forward_validation_before_device_work(lib):
+    args = ka.make_args(text_tokens=512, img_rows=64, img_cols=64, mode="tilemix")
+    q, k = _fake(48), _fake(12)
+    # TileMix needs a workspace
+    st = lib.attn_forward(ctypes.byref(args), ctypes.byref(q), ctypes.byref(k), ctypes.byref(k),
+                          ctypes.byref(q), None, 0, None)
+    assert st == -4
+    # misaligned and null tensors, bad strides
+    bad = ka.AttnTensor(0x100004, 4608 * 48 * 128, 48 * 128, 128)
+    st = lib.attn_forward(ctypes.byref(args), ctypes.byref(bad), ctypes.byref(k), ctypes.byref(k),
+                          ctypes.byref(q), None, 0, None)
+    assert st == -1
+    null = ka.AttnTensor(0, 0, 0, 0)
+    st = lib.attn_forward(ctypes.byref(args), ctypes.byref(null), ctypes.byref(k), ctypes.byref(k),
+                          ctypes.byref(q), None, 0, None)
+    assert st == -1
+    odd = ka.AttnTensor(0x100000, 4608 * 48 * 128, 48 * 128 + 4, 128)
+    st = lib.attn_forward(ctypes.byref(args), ctypes.byref(odd), ctypes.byref(k), ctypes.byref(k),
+                          ctypes.byref(q), None, 0, None)
+    assert st == -1
+    st = lib.attn_forward(None, ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), ctypes.byref(q), None, 0, None)
+    assert st == -1
+    # fp32 refused before anything else
+    a32 = ka.make_args(text_tokens=512, img_rows=64, img_cols=64, dtype="f32")
+    st = lib.attn_forward(ctypes.byref(a32), ctypes.byref(q), ctypes.byref(k), ctypes.byref(k),
+                          ctypes.byref(q), None, 0, None)
+    assert st == -2
+
+
+def test_route_and_mask_reject_wrong_mode(lib):
+    args = ka.make_args(text_tokens=512, img_rows=64, img_cols=64, mode="dense")
+    out = np.zeros((36, 36), np.uint8)
+    assert lib.attn_route_map(ctypes.byref(args), out.ctypes.data, 36) == -1
+    assert lib.attn_block_mask(ctypes.byref(args), out.ctypes.data, 36) == -1
+    tm = ka.make_args(text_tokens=512, img_rows=64, img_cols=64, mode="tilemix")
+    assert lib.attn_route_map(ctypes.byref(tm), out.ctypes.data, 35) == -1
+
+
+def test_status_strings(lib):
+    for code, text in ka.STATUS.items():
+        assert lib.attn_status_string(code).decode() == text
+
+
+def test_python_raises_loudly_without_library(tmp_path):
+    # a missing library is an error, never a silent fallback
+    saved = ka._lib
+    try:
+        ka._lib = None
+        with pytest.raises(ka.KreaAttnError):
+            ka.load_library(str(tmp_path / "nope.so"))
+    finally:
+        ka._lib = saved
