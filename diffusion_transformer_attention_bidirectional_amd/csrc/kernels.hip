@@ -2,10 +2,12 @@
 //
 // Fused attention ("Krea 2 TileMix Attention (FP16/INT8 tiles)", "What it actually
 // patches"): bidirectional online-softmax attention; GQA is resolved in the kernel --
-// one workgroup owns 64 query tokens of the 4 query heads that share one KV head
-// (one wave per head), so each K/V tile is staged once in LDS and read by all four.
+// one workgroup (8 waves) owns 64 query tokens of the 4 query heads that share one KV
+// head, each wave 32 queries of one head, so each K/V tile is staged once in LDS and
+// read by all eight.  Two waves per SIMD: one wave's softmax overlaps the other's MFMAs.
 //
-// Per wave, per step of 64 keys (all matrix products on MFMA 32x32 tiles):
+// Per wave, per step of 128 keys (one route / mask block; all matrix products on MFMA
+// 32x32 tiles, in four sub-blocks of 32 keys):
 //   S^T[key, q] = K Q^T            bf16/f16 MFMA (32x32x16), or i8 MFMA (32x32x32) on
 //                                  INT8-routed tiles, int32 accumulate
 //   online softmax per query       each lane owns one query column of S^T, so the row
@@ -41,11 +43,12 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kModeDense = 0, kModeTileMix = 1, kModeScan = 2;
-constexpr int QT = 64;          // query tokens per workgroup
-constexpr int KT = 64;          // keys per step
-constexpr int TILE_BYTES = KT * 256;     // one 64 x 128 bf16 tile
+constexpr int QT = 64;          // query tokens per workgroup (x 4 heads)
+constexpr int KT = 128;         // keys per step = one 128-token route / mask block
+constexpr int NWAVE = 8;        // waves per attention workgroup: 4 heads x 2 halves of 32 queries
+constexpr int TILE_BYTES = KT * 256;     // one 128 x 128 bf16 tile (32 KB)
 constexpr int V_OFF = TILE_BYTES;        // V tile after K in a stage
-constexpr int STAGE = 2 * TILE_BYTES;    // bytes of LDS per pipeline stage
+constexpr int STAGE = 2 * TILE_BYTES;    // bytes of LDS per pipeline stage (64 KB)
 constexpr float TAU = 8.0f;     // rescale O only when the running max grows by > 2^8
 
 // ---------------------------------------------------------------- layout helpers
@@ -101,13 +104,13 @@ __device__ __forceinline__ StepInfo step_info(const AttnParams& p, int qa, int e
   StepInfo s;
   int kb;
   if (MODE == kModeScan) {
-    const int e = p.cols_list[e0 + (i >> 1)];
+    const int e = p.cols_list[e0 + i];
     kb = e & 0xffff;
     s.partial = (e >> 16) != 0;
   } else {
-    kb = i >> 1;
+    kb = i;
   }
-  s.k0 = kb * 128 + (i & 1) * KT;
+  s.k0 = kb * KT;
   if (MODE != kModeScan) s.partial = s.k0 + KT > p.n;
   s.int8 = (MODE == kModeTileMix) && p.route != nullptr && p.route[qa * p.nb + kb] != 0;
   return s;
@@ -116,10 +119,10 @@ template <int MODE>
 __device__ __forceinline__ int step_count(const AttnParams& p, int qa, int* e0) {
   if (MODE == kModeScan) {
     *e0 = p.row_ptr[qa];
-    return 2 * (p.row_ptr[qa + 1] - *e0);
+    return p.row_ptr[qa + 1] - *e0;
   }
   *e0 = 0;
-  return 2 * p.nb;
+  return p.nb;
 }
 
 // ---------------------------------------------------------------- LDS layouts
@@ -140,33 +143,36 @@ __device__ __forceinline__ int qk_chunk(int s, int lh) { return 4 * (s >> 1) + 2
 
 __device__ __forceinline__ lds_void* as_lds(unsigned char* p) { return (lds_void*)p; }
 
-// HBM -> LDS for one step, by DMA; 16 bytes per lane per instruction, 1 KB per
-// instruction; each wave moves a quarter of the tiles.  Padding and out-of-range
-// keys read row 0 (finite data; their probabilities are zero).
-template <int MODE, bool WITH_V = true>
+// HBM -> LDS for one step, by DMA; 16 bytes per lane per instruction, 1 KB (4 rows) per
+// instruction; the NW waves of the workgroup share the instructions.  Padding and
+// out-of-range keys read row 0 (finite data; their probabilities are zero).
+template <int MODE, int NW, bool WITH_V = true>
 __device__ __forceinline__ void dma_stage(const AttnParams& p, int b, int g, const StepInfo& s,
                                           unsigned char* stage, int wave, int lane) {
   const uint16_t* kbase = (const uint16_t*)p.k.ptr + (int64_t)b * p.k.sb + (int64_t)g * p.k.sh;
   const uint16_t* vbase = (const uint16_t*)p.v.ptr + (int64_t)b * p.v.sb + (int64_t)g * p.v.sh;
+  constexpr int PER = (KT / 4) / NW;  // 1 KB blocks per wave per tile
+  if (WITH_V || !s.int8) {
 #pragma unroll
-  for (int i = 0; i < (WITH_V || !s.int8 ? 4 : 0); ++i) {
-    const int n = wave * 4 + i;
-    const int row = 4 * n + (lane >> 4);
-    const int c = (lane & 15) ^ swz16(row);
-    const int t = s.k0 + row;
-    const int ph = tok_valid<MODE>(p, t) ? tok_phys<MODE>(p, t) : 0;
-    if (!s.int8)
-      __builtin_amdgcn_global_load_lds(kbase + (int64_t)ph * p.k.st + c * 8, as_lds(stage + n * 1024), 16, 0, 0);
-    if (WITH_V)
-      __builtin_amdgcn_global_load_lds(vbase + (int64_t)ph * p.v.st + c * 8, as_lds(stage + V_OFF + n * 1024), 16,
-                                       0, 0);
+    for (int i = 0; i < PER; ++i) {
+      const int n = wave * PER + i;
+      const int row = 4 * n + (lane >> 4);
+      const int c = (lane & 15) ^ swz16(row);
+      const int t = s.k0 + row;
+      const int ph = tok_valid<MODE>(p, t) ? tok_phys<MODE>(p, t) : 0;
+      if (!s.int8)
+        __builtin_amdgcn_global_load_lds(kbase + (int64_t)ph * p.k.st + c * 8, as_lds(stage + n * 1024), 16, 0, 0);
+      if (WITH_V)
+        __builtin_amdgcn_global_load_lds(vbase + (int64_t)ph * p.v.st + c * 8, as_lds(stage + V_OFF + n * 1024), 16,
+                                         0, 0);
+    }
   }
   if (MODE == kModeTileMix && s.int8) {
-    const int8_t* kc = p.k_codes + (((int64_t)b * p.heads_kv + g) * p.nb + (s.k0 >> 7)) * (128 * 128) +
-                       (s.k0 & 127) * 128;
+    constexpr int PER8 = (KT / 8) / NW;
+    const int8_t* kc = p.k_codes + (((int64_t)b * p.heads_kv + g) * p.nb + (s.k0 >> 7)) * (128 * 128);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int n = wave * 2 + i;
+    for (int i = 0; i < PER8; ++i) {
+      const int n = wave * PER8 + i;
       const int row = 8 * n + (lane >> 3);
       const int c = (lane & 7) ^ swz8(row);
       __builtin_amdgcn_global_load_lds(kc + row * 128 + c * 16, as_lds(stage + n * 1024), 16, 0, 0);
@@ -175,8 +181,9 @@ __device__ __forceinline__ void dma_stage(const AttnParams& p, int b, int g, con
 }
 
 // V^T fragment (A operand of O^T += V^T P^T) for 32 channels 32 db .. and the 16 keys
-// of k-step (kb, k2): two transpose reads of 4 keys each, matching the key order of the
-// P^T B operand taken from the S^T accumulator (keys 16 k2 + 8 half + 4 (l/32) + 0..3).
+// of k-step (sub-block kb of 32 keys, k2): two transpose reads of 4 keys each, matching
+// the key order of the P^T B operand taken from the S^T accumulator (keys
+// 32 kb + 16 k2 + 8 half + 4 (l/32) + 0..3).
 __device__ __forceinline__ uint4 v_frag(const unsigned char* vbuf, int db, int kb, int k2, int lane) {
   const int key = 32 * kb + 16 * k2 + 4 * (lane >> 5) + ((lane & 15) >> 2);
   const int c = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
@@ -275,145 +282,114 @@ __device__ __forceinline__ void tile_coords(int n_qtiles, int n_hg, int* qt, int
 // ---------------------------------------------------------------- fused attention
 // Per-wave state carried across steps.
 struct WaveState {
-  f32x16 O[4][2];  // O^T accumulators: 4 channel blocks x 2 query blocks
-  float m[2], l[2];
+  f32x16 O[4];  // O^T accumulators: 4 channel blocks of 32 x the wave's 32 queries
+  float m, l;   // running max (log2 units) and this lane's half of the running sum
 };
 
-// One step of 64 keys on the current LDS stage, while the DMA for the next step fills
+// One step of 128 keys on the current LDS stage, while the DMA for the next step fills
 // the other stage.  The two stages are separate restrict-qualified pointers so the
 // compiler knows the DMA cannot alias the reads and does not wait for it here.
-template <bool BF16, int MODE>
+template <bool BF16, int MODE, bool PARTIAL>
 __device__ __forceinline__ void attn_step(const AttnParams& p, const unsigned char* __restrict__ buf,
                                           unsigned char* __restrict__ nbuf, const StepInfo& cur,
                                           const StepInfo& nxt, bool has_next, int b, int g, int wave, int lane,
-                                          const uint4 (&qf)[2][8], const uint4 (&q8f)[2][4],
-                                          const QInfo (&qinfo)[2], const float (&qadd)[2], float sq_l2,
-                                          WaveState& ws) {
+                                          const uint4 (&qf)[8], const uint4 (&q8f)[4], const QInfo& qinfo,
+                                          float qadd, float sq_l2, WaveState& ws) {
   const int lq = lane & 31, lh = lane >> 5;
-  if (has_next) dma_stage<MODE>(p, b, g, nxt, nbuf, wave, lane);
-  f32x16 (&O)[4][2] = ws.O;
-  float (&m)[2] = ws.m;
-  float (&l)[2] = ws.l;
-  // Two sub-blocks of 32 keys; within each, K and V fragments are shared by both
-  // 32-query blocks of the wave.
+  if (has_next) dma_stage<MODE, NWAVE>(p, b, g, nxt, nbuf, wave, lane);
+  const bool int8 = MODE == kModeTileMix && cur.int8;
+  const float mul = int8 ? sq_l2 * p.k_scale[((int64_t)b * p.heads_kv + g) * p.nb + (cur.k0 >> 7)] : p.scale_log2;
+  const float add = int8 ? qadd : 0.f;
+#pragma unroll 1
+  for (int kb = 0; kb < KT / 32; ++kb) {
+    // ---- scores S^T[key, q] for 32 keys x the wave's 32 queries
+    f32x16 S;
+    if (int8) {
+      i32x16 Si;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    // ---- scores S^T[key, q] for 32 keys x 2 query blocks of 32
-    f32x16 S[2];
-    float mul, add[2];
-    if (MODE == kModeTileMix && cur.int8) {
-      i32x16 Si[2];
+      for (int r = 0; r < 16; ++r) Si[r] = 0;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int s = 0; s < 4; ++s) Si = mma8(*(const uint4*)(buf + off128(32 * kb + lq, 2 * s + lh)), q8f[s], Si);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) Si[qb][r] = 0;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint4 a = *(const uint4*)(buf + off128(32 * kb + lq, 2 * s + lh));
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) Si[qb] = mma8(a, q8f[qb][s], Si[qb]);
-      }
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) S[qb][r] = (float)Si[qb][r];
-      mul = sq_l2 * p.k_scale[((int64_t)b * p.heads_kv + g) * p.nb + (cur.k0 >> 7)];
-      add[0] = qadd[0];
-      add[1] = qadd[1];
+      for (int r = 0; r < 16; ++r) S[r] = (float)Si[r];
     } else {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int r = 0; r < 16; ++r) S[r] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) S[qb][r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const uint4 a = *(const uint4*)(buf + off256(32 * kb + lq, qk_chunk(s, lh)));
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) S[qb] = mma16<BF16>(a, qf[qb][s], S[qb]);
-      }
-      mul = p.scale_log2;
-      add[0] = 0.f;
-      add[1] = 0.f;
+      for (int s = 0; s < 8; ++s)
+        S = mma16<BF16>(*(const uint4*)(buf + off256(32 * kb + lq, qk_chunk(s, lh))), qf[s], S);
     }
 
-    // ---- online softmax (log2 domain), one query per lane and query block
-    uint4 P[2][2];
+    // ---- online softmax (log2 domain), one query per lane; lanes l and l^32 hold the
+    // two halves of its 32 keys
+    float mx;
+    if (PARTIAL) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float mx;
-      if (cur.partial) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = cur.k0 + 32 * kb + 8 * (r >> 2) + 4 * lh + (r & 3);
-          S[qb][r] = admit<MODE>(p, qinfo[qb], j) ? fmaf(S[qb][r], mul, add[qb]) : -INFINITY;
-        }
-        mx = S[qb][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[qb][r]);
-      } else {
-        float raw = S[qb][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) raw = fmaxf(raw, S[qb][r]);
-        mx = fmaf(raw, mul, add[qb]);
+      for (int r = 0; r < 16; ++r) {
+        const int j = cur.k0 + 32 * kb + 8 * (r >> 2) + 4 * lh + (r & 3);
+        S[r] = admit<MODE>(p, qinfo, j) ? fmaf(S[r], mul, add) : -INFINITY;
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[qb], mx);
-      const bool resc = mnew > m[qb] + TAU;
-      const float alpha = resc ? exp2f(m[qb] - mnew) : 1.0f;
-      if (resc) m[qb] = mnew;
-      const float muse = (m[qb] == -INFINITY) ? 0.f : m[qb];
-      float ls = 0.f;
-      if (cur.partial) {
+      mx = S[0];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          S[qb][r] = exp2f(S[qb][r] - muse);
-          ls += S[qb][r];
-        }
-      } else {
-        const float c = add[qb] - muse;
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+    } else {
+      float raw = S[0];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          S[qb][r] = exp2f(fmaf(S[qb][r], mul, c));
-          ls += S[qb][r];
-        }
+      for (int r = 1; r < 16; ++r) raw = fmaxf(raw, S[r]);
+      mx = fmaf(raw, mul, add);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(ws.m, mx);
+    const bool resc = mnew > ws.m + TAU;
+    const float alpha = resc ? __builtin_amdgcn_exp2f(ws.m - mnew) : 1.0f;
+    if (resc) ws.m = mnew;
+    const float muse = (ws.m == -INFINITY) ? 0.f : ws.m;
+    float ls = 0.f;
+    if (PARTIAL) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        S[r] = __builtin_amdgcn_exp2f(S[r] - muse);
+        ls += S[r];
       }
-      l[qb] = l[qb] * alpha + ls;
-      if (__any(resc)) {
+    } else {
+      const float c = add - muse;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) O[db][qb][r] *= alpha;
+      for (int r = 0; r < 16; ++r) {
+        S[r] = __builtin_amdgcn_exp2f(fmaf(S[r], mul, c));
+        ls += S[r];
       }
+    }
+    ws.l = ws.l * alpha + ls;
+    if (__any(resc)) {
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const int r0 = 8 * k2;
-        P[qb][k2] = make_uint4(pack2<BF16>(S[qb][r0], S[qb][r0 + 1]), pack2<BF16>(S[qb][r0 + 2], S[qb][r0 + 3]),
-                               pack2<BF16>(S[qb][r0 + 4], S[qb][r0 + 5]),
-                               pack2<BF16>(S[qb][r0 + 6], S[qb][r0 + 7]));
-      }
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ws.O[db][r] *= alpha;
+    }
+    uint4 P[2];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int r0 = 8 * k2;
+      P[k2] = make_uint4(pack2<BF16>(S[r0], S[r0 + 1]), pack2<BF16>(S[r0 + 2], S[r0 + 3]),
+                         pack2<BF16>(S[r0 + 4], S[r0 + 5]), pack2<BF16>(S[r0 + 6], S[r0 + 7]));
     }
 
     // ---- O^T[d, q] += V^T[d, key] P^T[key, q] over these 32 keys (two k-steps of 16)
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const uint4 a = v_frag(buf + V_OFF, db, kb, k2, lane);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) O[db][qb] = mma16<BF16>(a, P[qb][k2], O[db][qb]);
-      }
+      for (int db = 0; db < 4; ++db) ws.O[db] = mma16<BF16>(v_frag(buf + V_OFF, db, kb, k2, lane), P[k2], ws.O[db]);
   }
-
 }
 
 template <bool BF16, int MODE>
-__global__ void __launch_bounds__(256) attn_fwd_kernel(const AttnParams p) {
+__global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, lh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int qt, hg, b;
   tile_coords((p.q_end - p.q_begin + QT - 1) / QT, p.heads_q / 4, &qt, &hg, &b);
-  const int h = hg * 4 + wave;
+  const int h = hg * 4 + (wave & 3);
   const int g = (hg * 4) / p.group;
   const int q0 = p.q_begin + qt * QT;
   const int qa = q0 >> 7;
@@ -424,46 +400,40 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const AttnParams p) {
                                          : (lo < min(hi, p.text)) || (max(lo, p.t_pad) < min(hi, p.t_pad + p.image));
     if (!any) return;
   }
+  const int tq = q0 + 32 * (wave >> 2) + lq;  // this lane's query (logical position)
 
-  uint4 qf[2][8];
-  load_q_frags<MODE>(p, b, h, q0 + lq, qf[0]);
-  load_q_frags<MODE>(p, b, h, q0 + 32 + lq, qf[1]);
-  const QInfo qinfo[2] = {query_info<MODE>(p, q0 + lq), query_info<MODE>(p, q0 + 32 + lq)};
+  uint4 qf[8];
+  load_q_frags<MODE>(p, b, h, tq, qf);
+  const QInfo qinfo = query_info<MODE>(p, tq);
 
   // TileMix: INT8 codes of this query block, and the smooth_k row term.  Raw K is used on
   // FP16 tiles and mean-centred codes on INT8 tiles; adding scale * q . mean to every INT8
   // score puts both on the same per-row offset, which softmax ignores (smooth_k is exact
   // for softmax, "The inputs that matter").
-  uint4 q8f[2][4];
-  float qadd[2] = {0.f, 0.f};
-  float sq_l2 = 0.f;
+  uint4 q8f[4];
+  float qadd = 0.f, sq_l2 = 0.f;
   if (MODE == kModeTileMix && p.q_inv != nullptr) {
     const int qidx = (b * p.heads_q + h) * p.nb + qa;
     const float inv = p.q_inv[qidx];
     sq_l2 = p.scale_log2 * p.q_scale[qidx];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) q8f[qb][s] = make_q8<BF16>(qf[qb][2 * s], qf[qb][2 * s + 1], inv);
+    for (int s = 0; s < 4; ++s) q8f[s] = make_q8<BF16>(qf[2 * s], qf[2 * s + 1], inv);
     if (p.smooth_k) {
       const float* mean = p.k_mean + ((int64_t)b * p.heads_kv + g) * 128;
+      float acc = 0.f;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float acc = 0.f;
+      for (int s = 0; s < 8; ++s) {
+        const uint4 x = qf[s];
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+        const float* mc = mean + 8 * qk_chunk(s, lh);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const uint4 x = qf[qb][s];
-          const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-          const float* mc = mean + 8 * qk_chunk(s, lh);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint16_t bits = (e & 1) ? (uint16_t)(w[e >> 1] >> 16) : (uint16_t)(w[e >> 1] & 0xffff);
-            acc = fmaf(elem_to_f32<BF16>(bits), mc[e], acc);
-          }
+        for (int e = 0; e < 8; ++e) {
+          const uint16_t bits = (e & 1) ? (uint16_t)(w[e >> 1] >> 16) : (uint16_t)(w[e >> 1] & 0xffff);
+          acc = fmaf(elem_to_f32<BF16>(bits), mc[e], acc);
         }
-        acc += __shfl_xor(acc, 32);
-        qadd[qb] = p.scale_log2 * acc;
       }
+      acc += __shfl_xor(acc, 32);
+      qadd = p.scale_log2 * acc;
     }
   }
 
@@ -473,50 +443,50 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(const AttnParams p) {
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ws.O[db][qb][r] = 0.f;
-  ws.m[0] = ws.m[1] = -INFINITY;
-  ws.l[0] = ws.l[1] = 0.f;
+    for (int r = 0; r < 16; ++r) ws.O[db][r] = 0.f;
+  ws.m = -INFINITY;
+  ws.l = 0.f;
 
   if (nsteps > 0) {
     StepInfo cur = step_info<MODE>(p, qa, e0, 0);
-    dma_stage<MODE>(p, b, g, cur, lds, wave, lane);
+    dma_stage<MODE, NWAVE>(p, b, g, cur, lds, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int i = 0; i < nsteps; ++i) {
       const bool has_next = i + 1 < nsteps;
       const StepInfo nxt = has_next ? step_info<MODE>(p, qa, e0, i + 1) : cur;
-      attn_step<BF16, MODE>(p, lds + (i & 1) * STAGE, lds + ((i + 1) & 1) * STAGE, cur, nxt, has_next, b, g, wave,
-                            lane, qf, q8f, qinfo, qadd, sq_l2, ws);
+      unsigned char* bcur = lds + (i & 1) * STAGE;
+      unsigned char* bnxt = lds + ((i + 1) & 1) * STAGE;
+      if (cur.partial)
+        attn_step<BF16, MODE, true>(p, bcur, bnxt, cur, nxt, has_next, b, g, wave, lane, qf, q8f, qinfo, qadd, sq_l2,
+                                    ws);
+      else
+        attn_step<BF16, MODE, false>(p, bcur, bnxt, cur, nxt, has_next, b, g, wave, lane, qf, q8f, qinfo, qadd, sq_l2,
+                                     ws);
       cur = nxt;
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
   }
-  const f32x16 (&O)[4][2] = ws.O;
-  const float (&l)[2] = ws.l;
 
   // ---- epilogue: O = O^T / l, rows of valid queries only (padding is never written)
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float lt = l[qb] + __shfl_xor(l[qb], 32);
-    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    const int t = q0 + 32 * qb + lq;
-    if (!qinfo[qb].valid) continue;
-    uint16_t* dst = (uint16_t*)p.o + (int64_t)b * p.o_sb + (int64_t)tok_phys<MODE>(p, t) * p.o_st +
+  const float lt = ws.l + __shfl_xor(ws.l, 32);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  if (qinfo.valid) {
+    uint16_t* dst = (uint16_t*)p.o + (int64_t)b * p.o_sb + (int64_t)tok_phys<MODE>(p, tq) * p.o_st +
                     (int64_t)h * p.o_sh;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
-        const f32x16& o = O[db][qb];
+        const f32x16& o = ws.O[db];
         const uint2 val = make_uint2(pack2<BF16>(o[4 * grp] * inv, o[4 * grp + 1] * inv),
                                      pack2<BF16>(o[4 * grp + 2] * inv, o[4 * grp + 3] * inv));
         *(uint2*)(dst + 32 * db + 8 * grp + 4 * lh) = val;
       }
   }
 }
+
 // ---------------------------------------------------------------- quantiser
 // TileMix INT8 stage ("Krea 2 TileMix Attention (FP16/INT8 tiles)", "The inputs that
 // matter": smooth_k mean-centres K per head before quantisation).  Reproducible rule:
@@ -657,7 +627,7 @@ __global__ void __launch_bounds__(256) q_codes_kernel(const QuantParams p, int8_
 // 32 w .. 32 w + 31 of the tile.
 template <bool BF16>
 __global__ void __launch_bounds__(256) int8_scores_kernel(const AttnParams p, const int32_t* tiles, int32_t* out) {
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[KT * 128];
   const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, lh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int* tl = tiles + 4 * blockIdx.x;
@@ -669,32 +639,25 @@ __global__ void __launch_bounds__(256) int8_scores_kernel(const AttnParams p, co
   uint4 q8f[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) q8f[s] = make_q8<BF16>(qf[2 * s], qf[2 * s + 1], inv);
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    StepInfo si;
-    si.k0 = kb * 128 + half * KT;
-    si.partial = false;
-    si.int8 = true;
-    dma_stage<kModeTileMix, false>(p, b, g, si, lds + half * STAGE, wave, lane);
-  }
+  StepInfo si;
+  si.k0 = kb * KT;
+  si.partial = false;
+  si.int8 = true;
+  dma_stage<kModeTileMix, 4, false>(p, b, g, si, lds, wave, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   int32_t* dst = out + (int64_t)blockIdx.x * 128 * 128;
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const unsigned char* buf = lds + half * STAGE;
+  for (int kb2 = 0; kb2 < KT / 32; ++kb2) {
+    i32x16 Si;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      i32x16 Si;
+    for (int r = 0; r < 16; ++r) Si[r] = 0;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) Si[r] = 0;
+    for (int s = 0; s < 4; ++s) Si = mma8(*(const uint4*)(lds + off128(32 * kb2 + lq, 2 * s + lh)), q8f[s], Si);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) Si = mma8(*(const uint4*)(buf + off128(32 * kb2 + lq, 2 * s + lh)), q8f[s], Si);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = half * KT + 32 * kb2 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        dst[(32 * wave + lq) * 128 + key] = Si[r];
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * kb2 + 8 * (r >> 2) + 4 * lh + (r & 3);
+      dst[(32 * wave + lq) * 128 + key] = Si[r];
     }
   }
 }
@@ -750,7 +713,7 @@ hipError_t launch_q_codes(const QuantParams& p, int8_t* q_codes, hipStream_t s) 
 template <bool BF16, int MODE>
 static void launch_attn_t(const AttnParams& p, hipStream_t s) {
   const int tiles = (p.q_end - p.q_begin + QT - 1) / QT * (p.heads_q / 4) * p.batch;
-  hipLaunchKernelGGL((attn_fwd_kernel<BF16, MODE>), dim3(tiles), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<BF16, MODE>), dim3(tiles), dim3(64 * NWAVE), 0, s, p);
 }
 
 hipError_t launch_attention(const AttnParams& p, int mode, bool bf16, hipStream_t s) {
