@@ -126,56 +126,74 @@ __device__ __forceinline__ int step_count(const AttnParams& p, int qa, int* e0) 
 }
 
 // ---------------------------------------------------------------- LDS layouts
-// bf16/f16 tiles (K and V): 64 rows x 256 B, row-major, 16-byte chunks XOR-swizzled by
-// a bijection of the row's low 4 bits.  Conflict-free for both the K fragment reads
-// (16 consecutive rows, one chunk) and the V transpose reads (4 consecutive rows,
-// 4 consecutive chunks).
-__device__ __forceinline__ int swz16(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
-__device__ __forceinline__ int off256(int row, int chunk) { return row * 256 + ((chunk ^ swz16(row)) << 4); }
-// INT8 K tile: 64 rows x 128 B; rows of equal parity spread over the 8 chunk slots.
-__device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
-__device__ __forceinline__ int off128(int row, int chunk) { return row * 128 + ((chunk ^ swz8(row)) << 4); }
+// A 128-key tile of K or V (128 x 128 bf16, 32 KB) is stored as 4 slabs, one per group of
+// 32 channels, each [128 rows][64 B] (four 16-byte chunks).  Every fragment read then has
+// a lane-dependent base and compile-time offsets for the slab, the key block and the step.
+//   V: no swizzle -- a transpose-read group touches 4 consecutive rows x 64 B = 256
+//      contiguous bytes, all banks once.
+//   K: the chunk is XORed with bits 2..3 of the row, so the 16 consecutive rows of a
+//      fragment read (same logical chunk) land on 16 distinct 16-byte bank slots.
+// INT8 K tile (128 x 128 B): 4 slabs, one per 32-channel k-step, each [128 rows][32 B];
+// the chunk is XORed with bit 3 of the row for the same reason.
+constexpr int SLAB = 128 * 64;    // bytes per bf16 slab
+constexpr int SLAB8 = 128 * 32;   // bytes per INT8 slab
+__device__ __forceinline__ int k_swz(int row) { return (row >> 2) & 3; }
+__device__ __forceinline__ int k8_swz(int row) { return (row >> 3) & 1; }
 // Channel chunk (8 channels) a lane holds in k-step s of the bf16 Q K^T product.  Any
 // bijection works if Q and K agree; this one makes two consecutive steps cover 16
 // contiguous channels per lane, so the INT8 Q codes built from them line up with the
 // natural 16-byte chunks of the INT8 K rows.
 __device__ __forceinline__ int qk_chunk(int s, int lh) { return 4 * (s >> 1) + 2 * lh + (s & 1); }
+// Byte offset of the K fragment (key block kb of 32 rows, k-step s) for this lane.
+__device__ __forceinline__ int k_frag_off(int kb, int s, int lq, int lh) {
+  const int row = 32 * kb + lq;
+  return (s >> 1) * SLAB + row * 64 + (((2 * lh + (s & 1)) ^ k_swz(row)) << 4);
+}
+__device__ __forceinline__ int k8_frag_off(int kb, int s, int lq, int lh) {
+  const int row = 32 * kb + lq;
+  return s * SLAB8 + row * 32 + ((lh ^ k8_swz(row)) << 4);
+}
 
 __device__ __forceinline__ lds_void* as_lds(unsigned char* p) { return (lds_void*)p; }
 
-// HBM -> LDS for one step, by DMA; 16 bytes per lane per instruction, 1 KB (4 rows) per
-// instruction; the NW waves of the workgroup share the instructions.  Padding and
-// out-of-range keys read row 0 (finite data; their probabilities are zero).
+// HBM -> LDS for one step, by DMA; 16 bytes per lane per instruction, 1 KB per
+// instruction (16 rows of one slab; 32 rows for INT8); the NW waves of the workgroup
+// share the instructions.  Padding and out-of-range keys read row 0 (finite data; their
+// probabilities are zero).
 template <int MODE, int NW, bool WITH_V = true>
 __device__ __forceinline__ void dma_stage(const AttnParams& p, int b, int g, const StepInfo& s,
                                           unsigned char* stage, int wave, int lane) {
   const uint16_t* kbase = (const uint16_t*)p.k.ptr + (int64_t)b * p.k.sb + (int64_t)g * p.k.sh;
   const uint16_t* vbase = (const uint16_t*)p.v.ptr + (int64_t)b * p.v.sb + (int64_t)g * p.v.sh;
-  constexpr int PER = (KT / 4) / NW;  // 1 KB blocks per wave per tile
+  constexpr int PER = (4 * SLAB / 1024) / NW;  // 1 KB blocks per wave per tile
   if (WITH_V || !s.int8) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int n = wave * PER + i;
-      const int row = 4 * n + (lane >> 4);
-      const int c = (lane & 15) ^ swz16(row);
+      const int slab = n >> 3;
+      const int row = (n & 7) * 16 + (lane >> 2);
+      const int pc = lane & 3;
       const int t = s.k0 + row;
       const int ph = tok_valid<MODE>(p, t) ? tok_phys<MODE>(p, t) : 0;
       if (!s.int8)
-        __builtin_amdgcn_global_load_lds(kbase + (int64_t)ph * p.k.st + c * 8, as_lds(stage + n * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(kbase + (int64_t)ph * p.k.st + (4 * slab + (pc ^ k_swz(row))) * 8,
+                                         as_lds(stage + n * 1024), 16, 0, 0);
       if (WITH_V)
-        __builtin_amdgcn_global_load_lds(vbase + (int64_t)ph * p.v.st + c * 8, as_lds(stage + V_OFF + n * 1024), 16,
-                                         0, 0);
+        __builtin_amdgcn_global_load_lds(vbase + (int64_t)ph * p.v.st + (4 * slab + pc) * 8,
+                                         as_lds(stage + V_OFF + n * 1024), 16, 0, 0);
     }
   }
   if (MODE == kModeTileMix && s.int8) {
-    constexpr int PER8 = (KT / 8) / NW;
+    constexpr int PER8 = (4 * SLAB8 / 1024) / NW;
     const int8_t* kc = p.k_codes + (((int64_t)b * p.heads_kv + g) * p.nb + (s.k0 >> 7)) * (128 * 128);
 #pragma unroll
     for (int i = 0; i < PER8; ++i) {
       const int n = wave * PER8 + i;
-      const int row = 8 * n + (lane >> 3);
-      const int c = (lane & 7) ^ swz8(row);
-      __builtin_amdgcn_global_load_lds(kc + row * 128 + c * 16, as_lds(stage + n * 1024), 16, 0, 0);
+      const int slab = n >> 2;
+      const int row = (n & 3) * 32 + (lane >> 1);
+      const int pc = lane & 1;
+      __builtin_amdgcn_global_load_lds(kc + row * 128 + (2 * slab + (pc ^ k8_swz(row))) * 16,
+                                       as_lds(stage + n * 1024), 16, 0, 0);
     }
   }
 }
@@ -183,14 +201,14 @@ __device__ __forceinline__ void dma_stage(const AttnParams& p, int b, int g, con
 // V^T fragment (A operand of O^T += V^T P^T) for 32 channels 32 db .. and the 16 keys
 // of k-step (sub-block kb of 32 keys, k2): two transpose reads of 4 keys each, matching
 // the key order of the P^T B operand taken from the S^T accumulator (keys
-// 32 kb + 16 k2 + 8 half + 4 (l/32) + 0..3).
+// 32 kb + 16 k2 + 8 half + 4 (l/32) + 0..3).  Source lane s of each 16-lane group reads
+// key (s / 4) of its four, channels 32 db + 16 (group & 1) + 4 (s & 3) .. + 3.
 __device__ __forceinline__ uint4 v_frag(const unsigned char* vbuf, int db, int kb, int k2, int lane) {
-  const int key = 32 * kb + 16 * k2 + 4 * (lane >> 5) + ((lane & 15) >> 2);
-  const int c = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const int within = 8 * (lane & 1);
-  unsigned char* base = (unsigned char*)vbuf;
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off256(key, c) + within));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off256(key + 8, c) + within));
+  const int row = 32 * kb + 16 * k2 + 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int pc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  unsigned char* base = (unsigned char*)vbuf + db * SLAB + row * 64 + pc * 16 + 8 * (lane & 1);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)base);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8 * 64));
   const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
   return make_uint4(l2.x, l2.y, h2.x, h2.y);
 }
@@ -289,6 +307,54 @@ struct WaveState {
 // One step of 128 keys on the current LDS stage, while the DMA for the next step fills
 // the other stage.  The two stages are separate restrict-qualified pointers so the
 // compiler knows the DMA cannot alias the reads and does not wait for it here.
+// Max of a value over the lane pair (l, l ^ 32): one VALU lane swap, no LDS round trip.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(x, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+
+// Sum of the two probabilities packed in one 32-bit word (bf16 or fp16 pair): the row sum
+// uses exactly the rounded values the P V product sees.
+template <bool BF16>
+__device__ __forceinline__ float pair_sum(uint32_t pk, float acc) {
+  if (BF16) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), one, acc, false);
+  } else {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), one, acc, false);
+  }
+}
+
+// Raw scores S^T[key, q] of one 32-key sub-block (unscaled; INT8 tiles as int32 -> f32).
+template <bool BF16, int MODE>
+__device__ __forceinline__ f32x16 qk_scores(const unsigned char* __restrict__ buf, bool int8, int kb, int lq, int lh,
+                                            const uint4 (&qf)[8], const uint4 (&q8f)[4]) {
+  f32x16 S;
+  if (MODE == kModeTileMix && int8) {
+    i32x16 Si;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Si[r] = 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) Si = mma8(*(const uint4*)(buf + k8_frag_off(kb, s, lq, lh)), q8f[s], Si);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[r] = (float)Si[r];
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      S = mma16<BF16>(*(const uint4*)(buf + k_frag_off(kb, s, lq, lh)), qf[s], S);
+  }
+  return S;
+}
+
+// One step of 128 keys on the current LDS stage, while the DMA for the next step fills
+// the other stage.  The two stages are separate restrict-qualified pointers so the
+// compiler knows the DMA cannot alias the reads and does not wait for it here.
+// Inside the step the four 32-key sub-blocks are software pipelined: the Q K^T MFMAs of
+// sub-block j + 1 are issued before the softmax of sub-block j, so they run on the matrix
+// cores while the same wave does the softmax on the vector ALU.
 template <bool BF16, int MODE, bool PARTIAL>
 __device__ __forceinline__ void attn_step(const AttnParams& p, const unsigned char* __restrict__ buf,
                                           unsigned char* __restrict__ nbuf, const StepInfo& cur,
@@ -300,25 +366,11 @@ __device__ __forceinline__ void attn_step(const AttnParams& p, const unsigned ch
   const bool int8 = MODE == kModeTileMix && cur.int8;
   const float mul = int8 ? sq_l2 * p.k_scale[((int64_t)b * p.heads_kv + g) * p.nb + (cur.k0 >> 7)] : p.scale_log2;
   const float add = int8 ? qadd : 0.f;
+  f32x16 S = qk_scores<BF16, MODE>(buf, int8, 0, lq, lh, qf, q8f);
 #pragma unroll 1
   for (int kb = 0; kb < KT / 32; ++kb) {
-    // ---- scores S^T[key, q] for 32 keys x the wave's 32 queries
-    f32x16 S;
-    if (int8) {
-      i32x16 Si;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) Si[r] = 0;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) Si = mma8(*(const uint4*)(buf + off128(32 * kb + lq, 2 * s + lh)), q8f[s], Si);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) S[r] = (float)Si[r];
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) S[r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        S = mma16<BF16>(*(const uint4*)(buf + off256(32 * kb + lq, qk_chunk(s, lh))), qf[s], S);
-    }
+    f32x16 Sn;
+    if (kb + 1 < KT / 32) Sn = qk_scores<BF16, MODE>(buf, int8, kb + 1, lq, lh, qf, q8f);
 
     // ---- online softmax (log2 domain), one query per lane; lanes l and l^32 hold the
     // two halves of its 32 keys
@@ -338,33 +390,19 @@ __device__ __forceinline__ void attn_step(const AttnParams& p, const unsigned ch
       for (int r = 1; r < 16; ++r) raw = fmaxf(raw, S[r]);
       mx = fmaf(raw, mul, add);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = pair_max(mx);
     const float mnew = fmaxf(ws.m, mx);
     const bool resc = mnew > ws.m + TAU;
     const float alpha = resc ? __builtin_amdgcn_exp2f(ws.m - mnew) : 1.0f;
     if (resc) ws.m = mnew;
     const float muse = (ws.m == -INFINITY) ? 0.f : ws.m;
-    float ls = 0.f;
     if (PARTIAL) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        S[r] = __builtin_amdgcn_exp2f(S[r] - muse);
-        ls += S[r];
-      }
+      for (int r = 0; r < 16; ++r) S[r] = __builtin_amdgcn_exp2f(S[r] - muse);
     } else {
       const float c = add - muse;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        S[r] = __builtin_amdgcn_exp2f(fmaf(S[r], mul, c));
-        ls += S[r];
-      }
-    }
-    ws.l = ws.l * alpha + ls;
-    if (__any(resc)) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ws.O[db][r] *= alpha;
+      for (int r = 0; r < 16; ++r) S[r] = __builtin_amdgcn_exp2f(fmaf(S[r], mul, c));
     }
     uint4 P[2];
 #pragma unroll
@@ -373,12 +411,28 @@ __device__ __forceinline__ void attn_step(const AttnParams& p, const unsigned ch
       P[k2] = make_uint4(pack2<BF16>(S[r0], S[r0 + 1]), pack2<BF16>(S[r0 + 2], S[r0 + 3]),
                          pack2<BF16>(S[r0 + 4], S[r0 + 5]), pack2<BF16>(S[r0 + 6], S[r0 + 7]));
     }
+    float ls = ws.l * alpha;
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      ls = pair_sum<BF16>(P[k2].x, ls);
+      ls = pair_sum<BF16>(P[k2].y, ls);
+      ls = pair_sum<BF16>(P[k2].z, ls);
+      ls = pair_sum<BF16>(P[k2].w, ls);
+    }
+    ws.l = ls;
+    if (__any(resc)) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ws.O[db][r] *= alpha;
+    }
 
     // ---- O^T[d, q] += V^T[d, key] P^T[key, q] over these 32 keys (two k-steps of 16)
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
       for (int db = 0; db < 4; ++db) ws.O[db] = mma16<BF16>(v_frag(buf + V_OFF, db, kb, k2, lane), P[k2], ws.O[db]);
+    S = Sn;
   }
 }
 
@@ -653,7 +707,7 @@ __global__ void __launch_bounds__(256) int8_scores_kernel(const AttnParams p, co
 #pragma unroll
     for (int r = 0; r < 16; ++r) Si[r] = 0;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) Si = mma8(*(const uint4*)(lds + off128(32 * kb2 + lq, 2 * s + lh)), q8f[s], Si);
+    for (int s = 0; s < 4; ++s) Si = mma8(*(const uint4*)(lds + k8_frag_off(kb2, s, lq, lh)), q8f[s], Si);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = 32 * kb2 + 8 * (r >> 2) + 4 * lh + (r & 3);
