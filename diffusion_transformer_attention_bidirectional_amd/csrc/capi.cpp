@@ -31,7 +31,7 @@ struct DevicePlan {
   int device = -1;
   krea::Plan plan;
   unsigned char* dmem = nullptr;
-  size_t route_off = 0, row_ptr_off = 0, cols_off = 0;
+  size_t route_off = 0, row_ptr_off = 0, cols_off = 0, full_off = 0;
   ~DevicePlan() {
     if (dmem) {
       int cur = 0;
@@ -71,6 +71,8 @@ attn_status get_plan(const attn_args& a, std::shared_ptr<DevicePlan>* out) {
   bytes += (p.row_ptr.size() * 4 + 255) & ~(size_t)255;
   dp->cols_off = bytes;
   bytes += (p.cols.size() * 4 + 255) & ~(size_t)255;
+  dp->full_off = bytes;
+  bytes += (p.full_count.size() * 4 + 255) & ~(size_t)255;
   if (bytes == 0) bytes = 256;
   if (hipMalloc((void**)&dp->dmem, bytes) != hipSuccess) {
     dp->dmem = nullptr;
@@ -82,6 +84,8 @@ attn_status get_plan(const attn_args& a, std::shared_ptr<DevicePlan>* out) {
     e = hipMemcpy(dp->dmem + dp->row_ptr_off, p.row_ptr.data(), p.row_ptr.size() * 4, hipMemcpyHostToDevice);
   if (e == hipSuccess && !p.cols.empty())
     e = hipMemcpy(dp->dmem + dp->cols_off, p.cols.data(), p.cols.size() * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess && !p.full_count.empty())
+    e = hipMemcpy(dp->dmem + dp->full_off, p.full_count.data(), p.full_count.size() * 4, hipMemcpyHostToDevice);
   if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, std::string("plan upload failed: ") + hipGetErrorString(e));
   if (std::getenv("KREA_ATTN_LOG")) {
     std::fprintf(stderr, "[krea_attn] plan built: mode %d, %d blocks, %lld INT8 tiles, %lld active, %lld partial\n",
@@ -142,6 +146,7 @@ krea::AttnParams make_params(const attn_args& a, const DevicePlan* dp) {
   if (!dp->plan.route.empty()) p.route = dp->dmem + dp->route_off;
   if (!dp->plan.row_ptr.empty()) p.row_ptr = (const int32_t*)(dp->dmem + dp->row_ptr_off);
   if (!dp->plan.cols.empty()) p.cols_list = (const int32_t*)(dp->dmem + dp->cols_off);
+  if (!dp->plan.full_count.empty()) p.full_count = (const int32_t*)(dp->dmem + dp->full_off);
   return p;
 }
 
@@ -195,8 +200,10 @@ attn_status attn_forward(const attn_args* args, const attn_tensor* q, const attn
       (s = check_tensor(o, "o")))
     return s;
   const attn_args& a = *args;
+  if (k->stride_t >= (1 << 23))
+    return fail(ATTN_ERR_INVALID_ARG, "k token stride must be below 2^23 elements (32-bit tile offsets)");
   const krea::WorkspaceLayout w = krea::workspace_layout(a);
-  if (w.total > 0 && (!workspace || workspace_bytes < w.total))
+  if (!workspace || workspace_bytes < w.total)
     return fail(ATTN_ERR_WORKSPACE, "workspace smaller than attn_workspace_bytes()");
   if (workspace && ((uintptr_t)workspace & 255)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   std::shared_ptr<DevicePlan> dp;
@@ -211,6 +218,9 @@ attn_status attn_forward(const attn_args* args, const attn_tensor* q, const attn
   p.o_st = o->stride_t;
   p.o_sh = o->stride_h;
   const bool bf16 = a.dtype == ATTN_BF16;
+  p.v_t = (const uint16_t*)((unsigned char*)workspace + w.v_t);
+  if ((s = hip_check(krea::launch_v_relayout(p, (uint16_t*)p.v_t, a.mode, st), "V relayout launch")) != ATTN_OK)
+    return s;
   if (a.mode == ATTN_TILEMIX) {
     if (dp->plan.int8_tiles > 0) {
       const krea::QuantParams qp = make_quant(a, q, k, (unsigned char*)workspace);

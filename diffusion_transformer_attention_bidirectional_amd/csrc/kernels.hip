@@ -13,9 +13,11 @@
 //   online softmax per query       each lane owns one query column of S^T, so the row
 //                                  max and sum stay in the lane (one swap with lane^32)
 //   O^T[d, q] += V^T P^T           bf16/f16 MFMA; P^T is the S^T accumulator converted
-//                                  in place; V^T fragments come from the row-major V
-//                                  tile through LDS transpose reads
-// K and V tiles move HBM -> LDS by DMA (global_load_lds), double buffered.
+//                                  in place; V^T comes from per-call V^T tiles that a
+//                                  relayout pass writes to the workspace, so every LDS
+//                                  fragment read is 16 bytes per lane (8-byte reads,
+//                                  transposed or not, run ~3x slower per byte on gfx950)
+// K and V^T tiles move HBM -> LDS by DMA (global_load_lds), double buffered.
 //
 // Hardware facts this file relies on (checked on gfx950):
 //   * MFMA 32x32 result: lane l holds column l % 32 and, in register r, row
@@ -149,6 +151,13 @@ __device__ __forceinline__ int k_frag_off(int kb, int s, int lq, int lh) {
   const int row = 32 * kb + lq;
   return (s >> 1) * SLAB + row * 64 + (((2 * lh + (s & 1)) ^ k_swz(row)) << 4);
 }
+// V^T tile in LDS: 4 slabs, one per 32-key sub-block, each [128 channel rows][64 B]: the
+// 16-byte chunk 2 k2 + lh of a row holds the 8 keys a P^T B-operand lane holds in k-step
+// k2 (keys 16 k2 + 8 (e / 4) + 4 lh + e % 4); swizzled like K.
+__device__ __forceinline__ int vt_frag_off(int db, int kb, int k2, int lq, int lh) {
+  const int d = 32 * db + lq;
+  return kb * SLAB + d * 64 + (((2 * k2 + lh) ^ k_swz(d)) << 4);
+}
 __device__ __forceinline__ int k8_frag_off(int kb, int s, int lq, int lh) {
   const int row = 32 * kb + lq;
   return s * SLAB8 + row * 32 + ((lh ^ k8_swz(row)) << 4);
@@ -158,34 +167,51 @@ __device__ __forceinline__ lds_void* as_lds(unsigned char* p) { return (lds_void
 
 // HBM -> LDS for one step, by DMA; 16 bytes per lane per instruction, 1 KB per
 // instruction (16 rows of one slab; 32 rows for INT8); the NW waves of the workgroup
-// share the instructions.  Padding and out-of-range keys read row 0 (finite data; their
-// probabilities are zero).
+// share the instructions.  K of a full tile is 128 consecutive tokens of the tensor, so
+// its addresses are one uniform base per step plus a per-lane 32-bit offset; a partial
+// tile clamps padding and out-of-range keys to row 0 (finite data; their probabilities
+// are zero).  V^T tiles are contiguous 32 KB blocks of the workspace.
 template <int MODE, int NW, bool WITH_V = true>
 __device__ __forceinline__ void dma_stage(const AttnParams& p, int b, int g, const StepInfo& s,
                                           unsigned char* stage, int wave, int lane) {
-  const uint16_t* kbase = (const uint16_t*)p.k.ptr + (int64_t)b * p.k.sb + (int64_t)g * p.k.sh;
-  const uint16_t* vbase = (const uint16_t*)p.v.ptr + (int64_t)b * p.v.sb + (int64_t)g * p.v.sh;
   constexpr int PER = (4 * SLAB / 1024) / NW;  // 1 KB blocks per wave per tile
-  if (WITH_V || !s.int8) {
+  const int64_t bg = (int64_t)b * p.heads_kv + g;
+  if (!s.int8) {
+    const char* kbase = (const char*)p.k.ptr + ((int64_t)b * p.k.sb + (int64_t)g * p.k.sh) * 2;
+    if (!s.partial) {
+      const char* kt = kbase + (int64_t)tok_phys<MODE>(p, s.k0) * p.k.st * 2;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int n = wave * PER + i;
+        const int row = (n & 7) * 16 + (lane >> 2);
+        const uint32_t off = (uint32_t)row * (uint32_t)(p.k.st * 2) + (4 * (n >> 3) + ((lane & 3) ^ k_swz(row))) * 16;
+        __builtin_amdgcn_global_load_lds(kt + off, as_lds(stage + n * 1024), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int n = wave * PER + i;
+        const int row = (n & 7) * 16 + (lane >> 2);
+        const int t = s.k0 + row;
+        const int ph = tok_valid<MODE>(p, t) ? tok_phys<MODE>(p, t) : 0;
+        __builtin_amdgcn_global_load_lds(kbase + ((int64_t)ph * p.k.st + (4 * (n >> 3) + ((lane & 3) ^ k_swz(row))) * 8) * 2,
+                                         as_lds(stage + n * 1024), 16, 0, 0);
+      }
+    }
+  }
+  if (WITH_V) {
+    const char* vt = (const char*)p.v_t + ((bg * p.nb + (s.k0 >> 7)) << 15);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int n = wave * PER + i;
-      const int slab = n >> 3;
-      const int row = (n & 7) * 16 + (lane >> 2);
-      const int pc = lane & 3;
-      const int t = s.k0 + row;
-      const int ph = tok_valid<MODE>(p, t) ? tok_phys<MODE>(p, t) : 0;
-      if (!s.int8)
-        __builtin_amdgcn_global_load_lds(kbase + (int64_t)ph * p.k.st + (4 * slab + (pc ^ k_swz(row))) * 8,
-                                         as_lds(stage + n * 1024), 16, 0, 0);
-      if (WITH_V)
-        __builtin_amdgcn_global_load_lds(vbase + (int64_t)ph * p.v.st + (4 * slab + pc) * 8,
-                                         as_lds(stage + V_OFF + n * 1024), 16, 0, 0);
+      const int d = (n & 7) * 16 + (lane >> 2);
+      const uint32_t off = d * 256 + (4 * (n >> 3) + ((lane & 3) ^ k_swz(d))) * 16;
+      __builtin_amdgcn_global_load_lds(vt + off, as_lds(stage + V_OFF + n * 1024), 16, 0, 0);
     }
   }
   if (MODE == kModeTileMix && s.int8) {
     constexpr int PER8 = (4 * SLAB8 / 1024) / NW;
-    const int8_t* kc = p.k_codes + (((int64_t)b * p.heads_kv + g) * p.nb + (s.k0 >> 7)) * (128 * 128);
+    const int8_t* kc = p.k_codes + (bg * p.nb + (s.k0 >> 7)) * (128 * 128);
 #pragma unroll
     for (int i = 0; i < PER8; ++i) {
       const int n = wave * PER8 + i;
@@ -198,8 +224,9 @@ __device__ __forceinline__ void dma_stage(const AttnParams& p, int b, int g, con
   }
 }
 
-// V^T fragment (A operand of O^T += V^T P^T) for 32 channels 32 db .. and the 16 keys
-// of k-step (sub-block kb of 32 keys, k2): two transpose reads of 4 keys each, matching
+// V^T fragment for 32 channels 32 db .. and the 16 keys of k-step (sub-block kb of 32
+// keys, k2), read from a row-major V tile in LDS (4 slabs of [128 keys][64 B], no
+// swizzle) by the relayout pass: two transpose reads of 4 keys each, matching
 // the key order of the P^T B operand taken from the S^T accumulator (keys
 // 32 kb + 16 k2 + 8 half + 4 (l/32) + 0..3).  Source lane s of each 16-lane group reads
 // key (s / 4) of its four, channels 32 db + 16 (group & 1) + 4 (s & 3) .. + 3.
@@ -369,6 +396,13 @@ __device__ __forceinline__ void attn_step(const AttnParams& p, const unsigned ch
   f32x16 S = qk_scores<BF16, MODE>(buf, int8, 0, lq, lh, qf, q8f);
 #pragma unroll 1
   for (int kb = 0; kb < KT / 32; ++kb) {
+    // V^T fragments of this sub-block first: their LDS latency is covered by the Q K^T
+    // of the next sub-block and the max reduction below.
+    uint4 vf[2][4];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) vf[k2][db] = *(const uint4*)(buf + V_OFF + vt_frag_off(db, kb, k2, lq, lh));
     f32x16 Sn;
     if (kb + 1 < KT / 32) Sn = qk_scores<BF16, MODE>(buf, int8, kb + 1, lq, lh, qf, q8f);
 
@@ -395,6 +429,12 @@ __device__ __forceinline__ void attn_step(const AttnParams& p, const unsigned ch
     const bool resc = mnew > ws.m + TAU;
     const float alpha = resc ? __builtin_amdgcn_exp2f(ws.m - mnew) : 1.0f;
     if (resc) ws.m = mnew;
+    if (__any(resc)) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ws.O[db][r] *= alpha;
+    }
     const float muse = (ws.m == -INFINITY) ? 0.f : ws.m;
     if (PARTIAL) {
 #pragma unroll
@@ -420,19 +460,13 @@ __device__ __forceinline__ void attn_step(const AttnParams& p, const unsigned ch
       ls = pair_sum<BF16>(P[k2].w, ls);
     }
     ws.l = ls;
-    if (__any(resc)) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ws.O[db][r] *= alpha;
-    }
 
     // ---- O^T[d, q] += V^T[d, key] P^T[key, q] over these 32 keys (two k-steps of 16)
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) ws.O[db] = mma16<BF16>(v_frag(buf + V_OFF, db, kb, k2, lane), P[k2], ws.O[db]);
-    S = Sn;
+      for (int db = 0; db < 4; ++db) ws.O[db] = mma16<BF16>(vf[k2][db], P[k2], ws.O[db]);
+    if (kb + 1 < KT / 32) S = Sn;
   }
 }
 
@@ -506,17 +540,23 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
     dma_stage<MODE, NWAVE>(p, b, g, cur, lds, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int i = 0; i < nsteps; ++i) {
+    // full tiles first, then the partial ones (padding, ragged tail, exact scanline
+    // rule) with the element mask: two loops, so the lean one keeps its registers
+    const int nfull = MODE == kModeScan ? p.full_count[qa] : (p.n % KT ? nsteps - 1 : nsteps);
+    for (int i = 0; i < nfull; ++i) {
       const bool has_next = i + 1 < nsteps;
       const StepInfo nxt = has_next ? step_info<MODE>(p, qa, e0, i + 1) : cur;
-      unsigned char* bcur = lds + (i & 1) * STAGE;
-      unsigned char* bnxt = lds + ((i + 1) & 1) * STAGE;
-      if (cur.partial)
-        attn_step<BF16, MODE, true>(p, bcur, bnxt, cur, nxt, has_next, b, g, wave, lane, qf, q8f, qinfo, qadd, sq_l2,
-                                    ws);
-      else
-        attn_step<BF16, MODE, false>(p, bcur, bnxt, cur, nxt, has_next, b, g, wave, lane, qf, q8f, qinfo, qadd, sq_l2,
-                                     ws);
+      attn_step<BF16, MODE, false>(p, lds + (i & 1) * STAGE, lds + ((i + 1) & 1) * STAGE, cur, nxt, has_next, b, g,
+                                   wave, lane, qf, q8f, qinfo, qadd, sq_l2, ws);
+      cur = nxt;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+    for (int i = nfull; i < nsteps; ++i) {
+      const bool has_next = i + 1 < nsteps;
+      const StepInfo nxt = has_next ? step_info<MODE>(p, qa, e0, i + 1) : cur;
+      attn_step<BF16, MODE, true>(p, lds + (i & 1) * STAGE, lds + ((i + 1) & 1) * STAGE, cur, nxt, has_next, b, g,
+                                  wave, lane, qf, q8f, qinfo, qadd, sq_l2, ws);
       cur = nxt;
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -539,6 +579,36 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
         *(uint2*)(dst + 32 * db + 8 * grp + 4 * lh) = val;
       }
   }
+}
+
+// ---------------------------------------------------------------- V^T relayout
+// Writes V^T tiles [B, Hkv, nb, 128 channels, 128 keys] for the attention kernel: logical
+// key order (scanline padding is zero), keys of each 16-key group in P^T order.  One
+// workgroup per (batch, KV head, 128-key block); the tile goes through LDS row-major and
+// comes back through transpose reads as exactly the fragments the attention kernel reads.
+template <int MODE>
+__global__ void __launch_bounds__(256) v_relayout_kernel(const AttnParams p, uint16_t* v_t) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * SLAB];
+  const int kb = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int lane = tid & 63, lq = lane & 31, lh = lane >> 5;
+  const uint16_t* vbase = (const uint16_t*)p.v.ptr + (int64_t)b * p.v.sb + (int64_t)g * p.v.sh;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int id = tid + 256 * i;
+    const int row = id >> 4, c = id & 15;
+    const int t = kb * KT + row;
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (tok_valid<MODE>(p, t)) x = *(const uint4*)(vbase + (int64_t)tok_phys<MODE>(p, t) * p.v.st + c * 8);
+    *(uint4*)(lds + (c >> 2) * SLAB + row * 64 + (c & 3) * 16) = x;
+  }
+  __syncthreads();
+  const int db = tid >> 6;
+  uint16_t* dst = v_t + ((((int64_t)b * p.heads_kv + g) * p.nb + kb) * 128 + 32 * db + lq) * 128;
+#pragma unroll
+  for (int kb2 = 0; kb2 < 4; ++kb2)
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+      *(uint4*)(dst + (4 * kb2 + 2 * k2 + lh) * 8) = v_frag(lds, db, kb2, k2, lane);
 }
 
 // ---------------------------------------------------------------- quantiser
@@ -780,6 +850,13 @@ hipError_t launch_attention(const AttnParams& p, int mode, bool bf16, hipStream_
     else if (mode == kModeTileMix) launch_attn_t<false, kModeTileMix>(p, s);
     else launch_attn_t<false, kModeScan>(p, s);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_v_relayout(const AttnParams& p, uint16_t* v_t, int mode, hipStream_t s) {
+  const dim3 grid(p.nb, p.heads_kv, p.batch);
+  if (mode == kModeScan) hipLaunchKernelGGL(v_relayout_kernel<kModeScan>, grid, dim3(256), 0, s, p, v_t);
+  else hipLaunchKernelGGL(v_relayout_kernel<kModeDense>, grid, dim3(256), 0, s, p, v_t);
   return hipGetLastError();
 }
 

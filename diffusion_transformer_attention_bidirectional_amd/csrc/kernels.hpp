@@ -34,11 +34,13 @@ struct AttnParams {
   const uint8_t* route;    // TileMix [nb * nb]
   const int32_t* row_ptr;  // scanline tile lists
   const int32_t* cols_list;
+  const int32_t* full_count;  // scanline: full tiles at the head of each list
   const float* k_mean;     // [B, Hkv, 128]
   const int8_t* k_codes;   // [B, Hkv, nb, 128, 128]
   const float* k_scale;    // [B, Hkv, nb]
   const float* q_inv;      // [B, Hq, nb]
   const float* q_scale;    // [B, Hq, nb]
+  const uint16_t* v_t;     // V^T tiles [B, Hkv, nb, 128 channels, 128 keys] (keys in P^T order)
 };
 
 // Quantiser stage for TileMix (smooth_k mean, K codes, Q scales).
@@ -57,6 +59,7 @@ struct QuantParams {
 
 hipError_t launch_quant(const QuantParams& p, hipStream_t s);
 hipError_t launch_attention(const AttnParams& p, int mode, bool bf16, hipStream_t s);
+hipError_t launch_v_relayout(const AttnParams& p, uint16_t* v_t, int mode, hipStream_t s);
 hipError_t launch_q_codes(const QuantParams& p, int8_t* q_codes, hipStream_t s);
 hipError_t launch_int8_scores(const AttnParams& p, const int32_t* tiles, int n_tiles, int32_t* out,
                               bool bf16, hipStream_t s);

@@ -124,10 +124,14 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 WorkspaceLayout workspace_layout(const attn_args& a) {
   WorkspaceLayout w;
-  if (a.mode != ATTN_TILEMIX) return w;
   const Layout l = make_layout(a);
   const size_t bk = (size_t)a.batch * a.heads_kv, bq = (size_t)a.batch * a.heads_q;
   size_t off = 0;
+  w.v_t = off;     off = align256(off + bk * l.nb * (size_t)kTile * kHeadDim * 2);
+  if (a.mode != ATTN_TILEMIX) {
+    w.total = off;
+    return w;
+  }
   w.k_part = off;  off = align256(off + bk * l.nb * kHeadDim * sizeof(double));
   w.k_mean = off;  off = align256(off + bk * kHeadDim * sizeof(float));
   w.k_codes = off; off = align256(off + bk * l.nb * (size_t)kTile * kHeadDim);
@@ -242,13 +246,17 @@ Plan build_plan(const attn_args& a) {
   } else if (a.mode == ATTN_SCANLINE) {
     p.bmask = build_block_mask(a, p.lay);
     p.row_ptr.assign(nb + 1, 0);
+    p.full_count.assign(nb, 0);
     for (int qa = 0; qa < nb; ++qa) {
-      for (int kb = 0; kb < nb; ++kb) {
-        const uint8_t v = p.bmask[(size_t)qa * nb + kb];
-        if (!v) continue;
-        p.cols.push_back(kb | ((v == 2) << 16));
-        ++p.active_tiles;
-        if (v == 2) ++p.partial_tiles;
+      for (int pass = 0; pass < 2; ++pass) {
+        for (int kb = 0; kb < nb; ++kb) {
+          const uint8_t v = p.bmask[(size_t)qa * nb + kb];
+          if (v != (pass == 0 ? 1 : 2)) continue;
+          p.cols.push_back(kb | ((v == 2) << 16));
+          ++p.active_tiles;
+          if (v == 2) ++p.partial_tiles;
+          else ++p.full_count[qa];
+        }
       }
       p.row_ptr[qa + 1] = (int32_t)p.cols.size();
     }

@@ -34,14 +34,19 @@ struct Plan {
   std::vector<uint8_t> route;    // TileMix [nb * nb], 1 = INT8
   std::vector<uint8_t> bmask;    // scanline [nb * nb], 0 skip / 1 full / 2 partial
   // Per query block tile list (scanline): entries of block a are
-  // cols[row_ptr[a] .. row_ptr[a + 1]), each (key block) | (partial << 16).
+  // cols[row_ptr[a] .. row_ptr[a + 1]), each (key block) | (partial << 16); the
+  // full_count[a] full tiles come first, then the partial ones (online softmax does not
+  // depend on the order, and the kernel runs the two kinds in separate loops).
   std::vector<int32_t> row_ptr;
   std::vector<int32_t> cols;
+  std::vector<int32_t> full_count;
   int64_t int8_tiles = 0, active_tiles = 0, partial_tiles = 0;
 };
 
-// Offsets of the TileMix workspace regions (bytes, 256-aligned).
+// Offsets of the workspace regions (bytes, 256-aligned).  Every mode holds V^T tiles
+// [B, Hkv, nb, 128 channels, 128 keys]; TileMix adds the quantiser state.
 struct WorkspaceLayout {
+  size_t v_t = 0;
   size_t k_part = 0, k_mean = 0, k_codes = 0, k_scale = 0, q_inv = 0, q_scale = 0;
   size_t total = 0;
 };

@@ -109,15 +109,17 @@ typedef struct {
   int64_t partial_tiles;  /* visited tiles that need element masking */
 } attn_plan_info;
 
-/* Bytes of device workspace attn_forward needs for these arguments (0 for dense and
- * scanline; TileMix holds the smooth_k partial sums and mean, INT8 K codes and scales,
- * and Q scales).  Host only. */
+/* Bytes of device workspace attn_forward needs for these arguments.  Every mode holds a
+ * relayout of V (V^T tiles of 128 keys, the size of V rounded up to whole tiles); TileMix
+ * adds the smooth_k partial sums and mean, INT8 K codes and scales, and Q scales.
+ * Host only. */
 attn_status attn_workspace_bytes(const attn_args* args, size_t* bytes);
 
 /* The attention call.  q, k, v are read, o is written (rows of every valid token;
  * padding never appears in o).  workspace: device memory of at least
- * attn_workspace_bytes() bytes (may be NULL when that is 0); its contents on entry
- * do not matter and are overwritten.  Enqueued on `stream` (a hipStream_t). */
+ * attn_workspace_bytes() bytes, 256-byte aligned; its contents on entry do not matter
+ * and are overwritten.  k's token stride must be below 2^23 elements.  Enqueued on
+ * `stream` (a hipStream_t). */
 attn_status attn_forward(const attn_args* args, const attn_tensor* q, const attn_tensor* k,
                          const attn_tensor* v, const attn_tensor* o, void* workspace,
                          size_t workspace_bytes, void* stream);

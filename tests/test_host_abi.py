@@ -113,13 +113,15 @@ def test_block_mask_4mp_vs_oracle(lib):
 
 
 def test_workspace_sizes(lib):
-    assert ka.workspace_bytes(ka.make_args(text_tokens=512, img_rows=64, img_cols=64)) == 0
-    scan = ka.make_args(text_tokens=512, img_rows=64, img_cols=64, mode="scanline")
-    assert ka.workspace_bytes(scan) == 0
+    # every mode: V^T tiles, 12 KV heads x 36 blocks x 128 x 128 bf16
+    vt = 12 * 36 * 128 * 128 * 2
+    assert ka.workspace_bytes(ka.make_args(text_tokens=512, img_rows=64, img_cols=64)) == vt
+    scan = ka.make_args(text_tokens=77, img_rows=10, img_cols=12, heads_q=4, heads_kv=1, mode="scanline")
+    assert ka.workspace_bytes(scan) == 2 * 128 * 128 * 2  # padded logical length 256
     tm = ka.make_args(text_tokens=512, img_rows=64, img_cols=64, mode="tilemix")
     n = ka.workspace_bytes(tm)
-    # at least the INT8 K codes: 12 KV heads x 36 blocks x 128 x 128
-    assert n >= 12 * 36 * 128 * 128
+    # plus at least the INT8 K codes: 12 KV heads x 36 blocks x 128 x 128
+    assert n >= vt + 12 * 36 * 128 * 128
 
 
 def _status(fn, *a):
@@ -164,7 +166,7 @@ def _fake(h):
 def test_forward_validation_before_device_work(lib):
     args = ka.make_args(text_tokens=512, img_rows=64, img_cols=64, mode="tilemix")
     q, k = _fake(48), _fake(12)
-    # TileMix needs a workspace
+    # every mode needs a workspace
     st = lib.attn_forward(ctypes.byref(args), ctypes.byref(q), ctypes.byref(k), ctypes.byref(k),
                           ctypes.byref(q), None, 0, None)
     assert st == -4
