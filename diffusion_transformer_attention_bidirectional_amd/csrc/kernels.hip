@@ -376,6 +376,87 @@ __device__ __forceinline__ f32x16 qk_scores(const unsigned char* __restrict__ bu
   return S;
 }
 
+// One 32-key sub-block: softmax of its scores S and O += V^T P^T; with NEXT, the Q K^T of
+// sub-block kb + 1 is issued first and returned in S (software pipelining: those MFMAs run
+// on the matrix cores while this wave does the softmax on the vector ALU).
+template <bool BF16, int MODE, bool PARTIAL, bool NEXT>
+__device__ __forceinline__ void attn_sub_block(const AttnParams& p, const unsigned char* __restrict__ buf,
+                                               const StepInfo& cur, bool int8, float mul, float add, int kb,
+                                               int lq, int lh, const uint4 (&qf)[8], const uint4 (&q8f)[4],
+                                               const QInfo& qinfo, f32x16& S, WaveState& ws) {
+  // V^T fragments of this sub-block first: their LDS latency is covered by the Q K^T
+  // of the next sub-block and the max reduction below.
+  uint4 vf[2][4];
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) vf[k2][db] = *(const uint4*)(buf + V_OFF + vt_frag_off(db, kb, k2, lq, lh));
+  f32x16 Sn;
+  if (NEXT) Sn = qk_scores<BF16, MODE>(buf, int8, kb + 1, lq, lh, qf, q8f);
+
+  // ---- online softmax (log2 domain), one query per lane; lanes l and l^32 hold the
+  // two halves of its 32 keys
+  float mx;
+  if (PARTIAL) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = cur.k0 + 32 * kb + 8 * (r >> 2) + 4 * lh + (r & 3);
+      S[r] = admit<MODE>(p, qinfo, j) ? fmaf(S[r], mul, add) : -INFINITY;
+    }
+    mx = S[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+  } else {
+    float raw = S[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) raw = fmaxf(raw, S[r]);
+    mx = fmaf(raw, mul, add);
+  }
+  mx = pair_max(mx);
+  const float mnew = fmaxf(ws.m, mx);
+  const bool resc = mnew > ws.m + TAU;
+  const float alpha = resc ? __builtin_amdgcn_exp2f(ws.m - mnew) : 1.0f;
+  if (resc) ws.m = mnew;
+  if (__any(resc)) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ws.O[db][r] *= alpha;
+  }
+  const float muse = (ws.m == -INFINITY) ? 0.f : ws.m;
+  if (PARTIAL) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[r] = __builtin_amdgcn_exp2f(S[r] - muse);
+  } else {
+    const float c = add - muse;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[r] = __builtin_amdgcn_exp2f(fmaf(S[r], mul, c));
+  }
+  uint4 P[2];
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+    const int r0 = 8 * k2;
+    P[k2] = make_uint4(pack2<BF16>(S[r0], S[r0 + 1]), pack2<BF16>(S[r0 + 2], S[r0 + 3]),
+                       pack2<BF16>(S[r0 + 4], S[r0 + 5]), pack2<BF16>(S[r0 + 6], S[r0 + 7]));
+  }
+  float ls = ws.l * alpha;
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+    ls = pair_sum<BF16>(P[k2].x, ls);
+    ls = pair_sum<BF16>(P[k2].y, ls);
+    ls = pair_sum<BF16>(P[k2].z, ls);
+    ls = pair_sum<BF16>(P[k2].w, ls);
+  }
+  ws.l = ls;
+
+  // ---- O^T[d, q] += V^T[d, key] P^T[key, q] over these 32 keys (two k-steps of 16)
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) ws.O[db] = mma16<BF16>(vf[k2][db], P[k2], ws.O[db]);
+  if (NEXT) S = Sn;
+}
+
 // One step of 128 keys on the current LDS stage, while the DMA for the next step fills
 // the other stage.  The two stages are separate restrict-qualified pointers so the
 // compiler knows the DMA cannot alias the reads and does not wait for it here.
@@ -395,79 +476,10 @@ __device__ __forceinline__ void attn_step(const AttnParams& p, const unsigned ch
   const float add = int8 ? qadd : 0.f;
   f32x16 S = qk_scores<BF16, MODE>(buf, int8, 0, lq, lh, qf, q8f);
 #pragma unroll 1
-  for (int kb = 0; kb < KT / 32; ++kb) {
-    // V^T fragments of this sub-block first: their LDS latency is covered by the Q K^T
-    // of the next sub-block and the max reduction below.
-    uint4 vf[2][4];
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) vf[k2][db] = *(const uint4*)(buf + V_OFF + vt_frag_off(db, kb, k2, lq, lh));
-    f32x16 Sn;
-    if (kb + 1 < KT / 32) Sn = qk_scores<BF16, MODE>(buf, int8, kb + 1, lq, lh, qf, q8f);
-
-    // ---- online softmax (log2 domain), one query per lane; lanes l and l^32 hold the
-    // two halves of its 32 keys
-    float mx;
-    if (PARTIAL) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = cur.k0 + 32 * kb + 8 * (r >> 2) + 4 * lh + (r & 3);
-        S[r] = admit<MODE>(p, qinfo, j) ? fmaf(S[r], mul, add) : -INFINITY;
-      }
-      mx = S[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-    } else {
-      float raw = S[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) raw = fmaxf(raw, S[r]);
-      mx = fmaf(raw, mul, add);
-    }
-    mx = pair_max(mx);
-    const float mnew = fmaxf(ws.m, mx);
-    const bool resc = mnew > ws.m + TAU;
-    const float alpha = resc ? __builtin_amdgcn_exp2f(ws.m - mnew) : 1.0f;
-    if (resc) ws.m = mnew;
-    if (__any(resc)) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ws.O[db][r] *= alpha;
-    }
-    const float muse = (ws.m == -INFINITY) ? 0.f : ws.m;
-    if (PARTIAL) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) S[r] = __builtin_amdgcn_exp2f(S[r] - muse);
-    } else {
-      const float c = add - muse;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) S[r] = __builtin_amdgcn_exp2f(fmaf(S[r], mul, c));
-    }
-    uint4 P[2];
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      const int r0 = 8 * k2;
-      P[k2] = make_uint4(pack2<BF16>(S[r0], S[r0 + 1]), pack2<BF16>(S[r0 + 2], S[r0 + 3]),
-                         pack2<BF16>(S[r0 + 4], S[r0 + 5]), pack2<BF16>(S[r0 + 6], S[r0 + 7]));
-    }
-    float ls = ws.l * alpha;
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      ls = pair_sum<BF16>(P[k2].x, ls);
-      ls = pair_sum<BF16>(P[k2].y, ls);
-      ls = pair_sum<BF16>(P[k2].z, ls);
-      ls = pair_sum<BF16>(P[k2].w, ls);
-    }
-    ws.l = ls;
-
-    // ---- O^T[d, q] += V^T[d, key] P^T[key, q] over these 32 keys (two k-steps of 16)
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) ws.O[db] = mma16<BF16>(vf[k2][db], P[k2], ws.O[db]);
-    if (kb + 1 < KT / 32) S = Sn;
-  }
+  for (int kb = 0; kb < KT / 32 - 1; ++kb)
+    attn_sub_block<BF16, MODE, PARTIAL, true>(p, buf, cur, int8, mul, add, kb, lq, lh, qf, q8f, qinfo, S, ws);
+  attn_sub_block<BF16, MODE, PARTIAL, false>(p, buf, cur, int8, mul, add, KT / 32 - 1, lq, lh, qf, q8f, qinfo, S,
+                                             ws);
 }
 
 template <bool BF16, int MODE>
