@@ -30,7 +30,7 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported dtype", -3: "unsuppo
 
 EXPORTS = ("attn_workspace_bytes", "attn_forward", "attn_plan_info_get", "attn_route_map",
            "attn_block_mask", "attn_quantize", "attn_int8_scores", "attn_mask_row_counts",
-           "attn_status_string", "attn_last_error")
+           "attn_set_kernel_events", "attn_status_string", "attn_last_error")
 
 
 class KreaAttnError(RuntimeError):
@@ -88,6 +88,7 @@ def load_library(path: str = LIB_PATH):
         "attn_quantize": [P(AttnArgs), P(AttnTensor), P(AttnTensor), vp, sz, vp, vp, vp, vp, vp, vp],
         "attn_int8_scores": [P(AttnArgs), P(AttnTensor), P(AttnTensor), vp, sz, vp, i32, vp, vp],
         "attn_mask_row_counts": [P(AttnArgs), vp, vp],
+        "attn_set_kernel_events": [vp, vp],
     }
     for name, argtypes in sig.items():
         fn = getattr(lib, name)
@@ -173,6 +174,15 @@ def attention(q, k, v, *, text_tokens, img_rows=0, img_cols=0, mode="dense", out
                                        ctypes.byref(_tensor(v)), ctypes.byref(_tensor(out)), wptr, wlen,
                                        _stream_handle(stream, q.device)))
     return out
+
+
+def set_kernel_events(start=None, stop=None):
+    """Record two recorded-once torch.cuda.Event objects around the attention-kernel
+    launches of every later attention() call on this thread; no arguments turns it off."""
+    if (start is None) != (stop is None):
+        raise KreaAttnError("give both events or neither")
+    ptr = (lambda e: None if e is None else ctypes.c_void_p(e.cuda_event))
+    _check(load_library().attn_set_kernel_events(ptr(start), ptr(stop)))
 
 
 # ---------------------------------------------------------------- host-only plan views

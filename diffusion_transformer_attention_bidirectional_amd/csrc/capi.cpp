@@ -18,6 +18,8 @@
 namespace {
 
 thread_local std::string g_err;
+// Measurement events recorded around the attention-kernel launches of attn_forward.
+thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
 
 attn_status fail(attn_status s, const std::string& msg) {
   g_err = msg;
@@ -237,11 +239,13 @@ attn_status attn_forward(const attn_args* args, const attn_tensor* q, const attn
   const int length = dp->plan.lay.length;
   const int chunk = a.q_chunk > 0 ? a.q_chunk : length;
   const int mode = a.mode;
+  if (g_ev_start && (s = hip_check(hipEventRecord(g_ev_start, st), "timing event")) != ATTN_OK) return s;
   for (int q0 = 0; q0 < length; q0 += chunk) {
     p.q_begin = q0;
     p.q_end = std::min(length, q0 + chunk);
     if ((s = hip_check(krea::launch_attention(p, mode, bf16, st), "attention launch")) != ATTN_OK) return s;
   }
+  if (g_ev_stop && (s = hip_check(hipEventRecord(g_ev_stop, st), "timing event")) != ATTN_OK) return s;
   g_err.clear();
   return ATTN_OK;
 }
@@ -348,6 +352,15 @@ attn_status attn_mask_row_counts(const attn_args* args, int32_t* out, void* stre
   if ((s = get_plan(*args, &dp)) != ATTN_OK) return s;
   const krea::AttnParams p = make_params(*args, dp.get());
   if ((s = hip_check(krea::launch_mask_counts(p, args->mode, out, (hipStream_t)stream), "launch"))) return s;
+  g_err.clear();
+  return ATTN_OK;
+}
+
+attn_status attn_set_kernel_events(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(ATTN_ERR_INVALID_ARG, "give both events or neither");
+  g_ev_start = (hipEvent_t)start_event;
+  g_ev_stop = (hipEvent_t)stop_event;
   g_err.clear();
   return ATTN_OK;
 }

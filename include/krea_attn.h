@@ -154,6 +154,14 @@ attn_status attn_int8_scores(const attn_args* args, const attn_tensor* q, const 
  * kernel's own tile list and element mask.  out: device int32 [logical_tokens]. */
 attn_status attn_mask_row_counts(const attn_args* args, int32_t* out, void* stream);
 
+/* Measurement hook.  With two hipEvent_t handles (created by the caller, who keeps
+ * ownership), every later attn_forward on the calling thread records start_event on its
+ * stream just before its first attention-kernel launch and stop_event just after its last
+ * one, so the span excludes the V relayout and the quantiser.  NULL, NULL turns it off;
+ * one NULL and one event is ATTN_ERR_INVALID_ARG.  A failed record makes attn_forward
+ * return ATTN_ERR_DEVICE.  Host only; enqueues nothing by itself. */
+attn_status attn_set_kernel_events(void* start_event, void* stop_event);
+
 const char* attn_status_string(attn_status status);
 /* Message for the last error on the calling thread ("" if none). */
 const char* attn_last_error(void);

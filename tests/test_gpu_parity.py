@@ -241,3 +241,29 @@ def test_krea_1mp_scanline_counts(dev):
                          tile_aligned=False)
     assert int(ka.mask_row_counts(args0, device=dev).cpu().numpy().sum()) == 7_217_152
     del w
+
+
+def test_kernel_events_hook(dev):
+    """The measurement hook brackets only the attention launches and leaves results unchanged."""
+    w = _w(mode="tilemix", pattern="band", percentage=0.5, band_blocks=1, smooth_k=True, q_chunk=128)
+    ref, (q, k, v) = _run(w, dev)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    stream = torch.cuda.current_stream(dev)
+    outer = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    inner = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for e in inner:
+        e.record(stream)
+    torch.cuda.synchronize()
+    try:
+        ka.set_kernel_events(*inner)
+        outer[0].record(stream)
+        out = ka.attention(qd, kd, vd, **_kw(w))
+        outer[1].record(stream)
+    finally:
+        ka.set_kernel_events()
+    torch.cuda.synchronize()
+    assert (out.float().cpu().numpy().astype(np.float64) == ref).all()
+    span, whole = inner[0].elapsed_time(inner[1]), outer[0].elapsed_time(outer[1])
+    assert 0.0 < span <= whole
+    with pytest.raises(ka.KreaAttnError):
+        ka.set_kernel_events(inner[0], None)
