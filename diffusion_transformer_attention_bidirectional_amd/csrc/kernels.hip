@@ -331,9 +331,6 @@ struct WaveState {
   float m, l;   // running max (log2 units) and this lane's half of the running sum
 };
 
-// One step of 128 keys on the current LDS stage, while the DMA for the next step fills
-// the other stage.  The two stages are separate restrict-qualified pointers so the
-// compiler knows the DMA cannot alias the reads and does not wait for it here.
 // Max of a value over the lane pair (l, l ^ 32): one VALU lane swap, no LDS round trip.
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -353,49 +350,62 @@ __device__ __forceinline__ float pair_sum(uint32_t pk, float acc) {
   }
 }
 
-// Raw scores S^T[key, q] of one 32-key sub-block (unscaled; INT8 tiles as int32 -> f32).
+// Raw scores S^T[key, q] of one 32-key sub-block: f32 on FP16 tiles, the int32
+// accumulators' bits on INT8 tiles (converted where the softmax reads them, so the
+// conversion never waits on the MFMA chain).
 template <bool BF16, int MODE>
 __device__ __forceinline__ f32x16 qk_scores(const unsigned char* __restrict__ buf, bool int8, int kb, int lq, int lh,
                                             const uint4 (&qf)[8], const uint4 (&q8f)[4]) {
-  f32x16 S;
   if (MODE == kModeTileMix && int8) {
     i32x16 Si;
 #pragma unroll
     for (int r = 0; r < 16; ++r) Si[r] = 0;
 #pragma unroll
     for (int s = 0; s < 4; ++s) Si = mma8(*(const uint4*)(buf + k8_frag_off(kb, s, lq, lh)), q8f[s], Si);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) S[r] = (float)Si[r];
-  } else {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) S[r] = 0.f;
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      S = mma16<BF16>(*(const uint4*)(buf + k_frag_off(kb, s, lq, lh)), qf[s], S);
+    return __builtin_bit_cast(f32x16, Si);
   }
+  f32x16 S;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) S[r] = 0.f;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) S = mma16<BF16>(*(const uint4*)(buf + k_frag_off(kb, s, lq, lh)), qf[s], S);
   return S;
 }
 
-// One 32-key sub-block: softmax of its scores S and O += V^T P^T; with NEXT, the Q K^T of
-// sub-block kb + 1 is issued first and returned in S (software pipelining: those MFMAs run
-// on the matrix cores while this wave does the softmax on the vector ALU).
-template <bool BF16, int MODE, bool PARTIAL, bool NEXT>
-__device__ __forceinline__ void attn_sub_block(const AttnParams& p, const unsigned char* __restrict__ buf,
-                                               const StepInfo& cur, bool int8, float mul, float add, int kb,
-                                               int lq, int lh, const uint4 (&qf)[8], const uint4 (&q8f)[4],
-                                               const QInfo& qinfo, f32x16& S, WaveState& ws) {
-  // V^T fragments of this sub-block first: their LDS latency is covered by the Q K^T
-  // of the next sub-block and the max reduction below.
-  uint4 vf[2][4];
+// Software pipeline over 32-key sub-blocks.  Sub-block j is handled in two scheduling
+// regions, so that every stretch of vector work has independent MFMAs beside it:
+//   A: O += V^T P^T of sub-block j - 1 (MFMA)   |  row max of S_j, lazy-rescale decision
+//   (rare branch: O *= alpha)
+//   B: S_{j+1} = K Q^T (MFMA)                   |  P_j = exp2(S_j), packing, row sums
+// At the last sub-block of a step the workgroup barrier (the next step's K/V^T tiles
+// have landed, this stage is free) sits between A and B, and the DMA of the step after
+// next is issued into the freed stage there.
+struct Pipe {
+  uint4 P[2];      // P^T of the previous sub-block (two k-steps of 16 keys, packed)
+  uint4 vf[2][4];  // V^T fragments of the previous sub-block
+};
+
+template <bool BF16, int MODE, bool PARTIAL, bool LAST>
+__device__ __forceinline__ void sub_block(const AttnParams& p, const unsigned char* __restrict__ buf,
+                                          unsigned char* __restrict__ nbuf, const StepInfo& cur,
+                                          const StepInfo& nxt, const StepInfo& nxt2, bool has_next, bool has_next2,
+                                          int b, int g, int wave, int lane, int kb, float mul, float add,
+                                          const uint4 (&qf)[8], const uint4 (&q8f)[4], const QInfo& qinfo,
+                                          f32x16& S, f32x16& Sn, Pipe& pp, WaveState& ws) {
+  const int lq = lane & 31, lh = lane >> 5;
+  // ---- region A
 #pragma unroll
   for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-    for (int db = 0; db < 4; ++db) vf[k2][db] = *(const uint4*)(buf + V_OFF + vt_frag_off(db, kb, k2, lq, lh));
-  f32x16 Sn;
-  if (NEXT) Sn = qk_scores<BF16, MODE>(buf, int8, kb + 1, lq, lh, qf, q8f);
-
-  // ---- online softmax (log2 domain), one query per lane; lanes l and l^32 hold the
-  // two halves of its 32 keys
+    for (int db = 0; db < 4; ++db) ws.O[db] = mma16<BF16>(pp.vf[k2][db], pp.P[k2], ws.O[db]);
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) pp.vf[k2][db] = *(const uint4*)(buf + V_OFF + vt_frag_off(db, kb, k2, lq, lh));
+  if (MODE == kModeTileMix && cur.int8) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[r] = (float)__float_as_int(S[r]);
+  }
   float mx;
   if (PARTIAL) {
 #pragma unroll
@@ -423,6 +433,18 @@ __device__ __forceinline__ void attn_sub_block(const AttnParams& p, const unsign
 #pragma unroll
       for (int r = 0; r < 16; ++r) ws.O[db][r] *= alpha;
   }
+  if (LAST) {
+    // every wave is done with this stage (its V^T reads above, its K reads one sub-block
+    // ago) and its own DMA of the next step has landed: after the barrier the next
+    // step's tiles are complete and this stage can take the step after next
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (has_next2) dma_stage<MODE, NWAVE>(p, b, g, nxt2, (unsigned char*)buf, wave, lane);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // ---- region B
+  if (!LAST) Sn = qk_scores<BF16, MODE>(buf, cur.int8, kb + 1, lq, lh, qf, q8f);
+  else if (has_next) Sn = qk_scores<BF16, MODE>(nbuf, nxt.int8, 0, lq, lh, qf, q8f);
   const float muse = (ws.m == -INFINITY) ? 0.f : ws.m;
   if (PARTIAL) {
 #pragma unroll
@@ -432,54 +454,46 @@ __device__ __forceinline__ void attn_sub_block(const AttnParams& p, const unsign
 #pragma unroll
     for (int r = 0; r < 16; ++r) S[r] = __builtin_amdgcn_exp2f(fmaf(S[r], mul, c));
   }
-  uint4 P[2];
 #pragma unroll
   for (int k2 = 0; k2 < 2; ++k2) {
     const int r0 = 8 * k2;
-    P[k2] = make_uint4(pack2<BF16>(S[r0], S[r0 + 1]), pack2<BF16>(S[r0 + 2], S[r0 + 3]),
-                       pack2<BF16>(S[r0 + 4], S[r0 + 5]), pack2<BF16>(S[r0 + 6], S[r0 + 7]));
+    pp.P[k2] = make_uint4(pack2<BF16>(S[r0], S[r0 + 1]), pack2<BF16>(S[r0 + 2], S[r0 + 3]),
+                          pack2<BF16>(S[r0 + 4], S[r0 + 5]), pack2<BF16>(S[r0 + 6], S[r0 + 7]));
   }
   float ls = ws.l * alpha;
 #pragma unroll
   for (int k2 = 0; k2 < 2; ++k2) {
-    ls = pair_sum<BF16>(P[k2].x, ls);
-    ls = pair_sum<BF16>(P[k2].y, ls);
-    ls = pair_sum<BF16>(P[k2].z, ls);
-    ls = pair_sum<BF16>(P[k2].w, ls);
+    ls = pair_sum<BF16>(pp.P[k2].x, ls);
+    ls = pair_sum<BF16>(pp.P[k2].y, ls);
+    ls = pair_sum<BF16>(pp.P[k2].z, ls);
+    ls = pair_sum<BF16>(pp.P[k2].w, ls);
   }
   ws.l = ls;
-
-  // ---- O^T[d, q] += V^T[d, key] P^T[key, q] over these 32 keys (two k-steps of 16)
-#pragma unroll
-  for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-    for (int db = 0; db < 4; ++db) ws.O[db] = mma16<BF16>(vf[k2][db], P[k2], ws.O[db]);
-  if (NEXT) S = Sn;
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-// One step of 128 keys on the current LDS stage, while the DMA for the next step fills
-// the other stage.  The two stages are separate restrict-qualified pointers so the
-// compiler knows the DMA cannot alias the reads and does not wait for it here.
-// Inside the step the four 32-key sub-blocks are software pipelined: the Q K^T MFMAs of
-// sub-block j + 1 are issued before the softmax of sub-block j, so they run on the matrix
-// cores while the same wave does the softmax on the vector ALU.
+// One step of 128 keys (four sub-blocks) on stage `buf`; the next step's tiles are in
+// `nbuf`.  On entry S0 holds the raw scores of this step's first sub-block; on exit it
+// holds those of the next step's first sub-block.  The two stages are separate
+// restrict-qualified pointers so the compiler knows the DMA cannot alias the reads.
 template <bool BF16, int MODE, bool PARTIAL>
 __device__ __forceinline__ void attn_step(const AttnParams& p, const unsigned char* __restrict__ buf,
                                           unsigned char* __restrict__ nbuf, const StepInfo& cur,
-                                          const StepInfo& nxt, bool has_next, int b, int g, int wave, int lane,
-                                          const uint4 (&qf)[8], const uint4 (&q8f)[4], const QInfo& qinfo,
-                                          float qadd, float sq_l2, WaveState& ws) {
-  const int lq = lane & 31, lh = lane >> 5;
-  if (has_next) dma_stage<MODE, NWAVE>(p, b, g, nxt, nbuf, wave, lane);
+                                          const StepInfo& nxt, const StepInfo& nxt2, bool has_next, bool has_next2,
+                                          int b, int g, int wave, int lane, const uint4 (&qf)[8],
+                                          const uint4 (&q8f)[4], const QInfo& qinfo, float qadd, float sq_l2,
+                                          f32x16& S0, f32x16& S1, Pipe& pp, WaveState& ws) {
   const bool int8 = MODE == kModeTileMix && cur.int8;
   const float mul = int8 ? sq_l2 * p.k_scale[((int64_t)b * p.heads_kv + g) * p.nb + (cur.k0 >> 7)] : p.scale_log2;
   const float add = int8 ? qadd : 0.f;
-  f32x16 S = qk_scores<BF16, MODE>(buf, int8, 0, lq, lh, qf, q8f);
-#pragma unroll 1
-  for (int kb = 0; kb < KT / 32 - 1; ++kb)
-    attn_sub_block<BF16, MODE, PARTIAL, true>(p, buf, cur, int8, mul, add, kb, lq, lh, qf, q8f, qinfo, S, ws);
-  attn_sub_block<BF16, MODE, PARTIAL, false>(p, buf, cur, int8, mul, add, KT / 32 - 1, lq, lh, qf, q8f, qinfo, S,
-                                             ws);
+  sub_block<BF16, MODE, PARTIAL, false>(p, buf, nbuf, cur, nxt, nxt2, has_next, has_next2, b, g, wave, lane, 0, mul,
+                                        add, qf, q8f, qinfo, S0, S1, pp, ws);
+  sub_block<BF16, MODE, PARTIAL, false>(p, buf, nbuf, cur, nxt, nxt2, has_next, has_next2, b, g, wave, lane, 1, mul,
+                                        add, qf, q8f, qinfo, S1, S0, pp, ws);
+  sub_block<BF16, MODE, PARTIAL, false>(p, buf, nbuf, cur, nxt, nxt2, has_next, has_next2, b, g, wave, lane, 2, mul,
+                                        add, qf, q8f, qinfo, S0, S1, pp, ws);
+  sub_block<BF16, MODE, PARTIAL, true>(p, buf, nbuf, cur, nxt, nxt2, has_next, has_next2, b, g, wave, lane, 3, mul,
+                                       add, qf, q8f, qinfo, S1, S0, pp, ws);
 }
 
 template <bool BF16, int MODE>
@@ -548,31 +562,46 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
   ws.l = 0.f;
 
   if (nsteps > 0) {
+    unsigned char* st0 = lds;
+    unsigned char* st1 = lds + STAGE;
     StepInfo cur = step_info<MODE>(p, qa, e0, 0);
-    dma_stage<MODE, NWAVE>(p, b, g, cur, lds, wave, lane);
+    StepInfo nxt = nsteps > 1 ? step_info<MODE>(p, qa, e0, 1) : cur;
+    dma_stage<MODE, NWAVE>(p, b, g, cur, st0, wave, lane);
+    if (nsteps > 1) dma_stage<MODE, NWAVE>(p, b, g, nxt, st1, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    Pipe pp;
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      pp.P[k2] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) pp.vf[k2][db] = make_uint4(0, 0, 0, 0);
+    }
+    f32x16 S0 = qk_scores<BF16, MODE>(st0, cur.int8, 0, lq, lh, qf, q8f), S1;
     // full tiles first, then the partial ones (padding, ragged tail, exact scanline
     // rule) with the element mask: two loops, so the lean one keeps its registers
     const int nfull = MODE == kModeScan ? p.full_count[qa] : (p.n % KT ? nsteps - 1 : nsteps);
     for (int i = 0; i < nfull; ++i) {
-      const bool has_next = i + 1 < nsteps;
-      const StepInfo nxt = has_next ? step_info<MODE>(p, qa, e0, i + 1) : cur;
-      attn_step<BF16, MODE, false>(p, lds + (i & 1) * STAGE, lds + ((i + 1) & 1) * STAGE, cur, nxt, has_next, b, g,
-                                   wave, lane, qf, q8f, qinfo, qadd, sq_l2, ws);
+      const bool has_next = i + 1 < nsteps, has_next2 = i + 2 < nsteps;
+      const StepInfo nxt2 = has_next2 ? step_info<MODE>(p, qa, e0, i + 2) : nxt;
+      attn_step<BF16, MODE, false>(p, (i & 1) ? st1 : st0, (i & 1) ? st0 : st1, cur, nxt, nxt2, has_next, has_next2,
+                                   b, g, wave, lane, qf, q8f, qinfo, qadd, sq_l2, S0, S1, pp, ws);
       cur = nxt;
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      nxt = nxt2;
     }
     for (int i = nfull; i < nsteps; ++i) {
-      const bool has_next = i + 1 < nsteps;
-      const StepInfo nxt = has_next ? step_info<MODE>(p, qa, e0, i + 1) : cur;
-      attn_step<BF16, MODE, true>(p, lds + (i & 1) * STAGE, lds + ((i + 1) & 1) * STAGE, cur, nxt, has_next, b, g,
-                                  wave, lane, qf, q8f, qinfo, qadd, sq_l2, ws);
+      const bool has_next = i + 1 < nsteps, has_next2 = i + 2 < nsteps;
+      const StepInfo nxt2 = has_next2 ? step_info<MODE>(p, qa, e0, i + 2) : nxt;
+      attn_step<BF16, MODE, true>(p, (i & 1) ? st1 : st0, (i & 1) ? st0 : st1, cur, nxt, nxt2, has_next, has_next2,
+                                  b, g, wave, lane, qf, q8f, qinfo, qadd, sq_l2, S0, S1, pp, ws);
       cur = nxt;
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      nxt = nxt2;
     }
+    // the last sub-block's P V
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) ws.O[db] = mma16<BF16>(pp.vf[k2][db], pp.P[k2], ws.O[db]);
   }
 
   // ---- epilogue: O = O^T / l, rows of valid queries only (padding is never written)
