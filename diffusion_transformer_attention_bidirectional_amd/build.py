@@ -23,8 +23,10 @@ LIB = os.path.join(PKG, "libkrea_attn.so")
 BUILD = os.path.join(PKG, "_build")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC, "-Wall"]
+# -fno-honor-nans: no kernel produces or consumes a NaN (masked scores are -inf and the
+# running max starts finite), so max reductions need no NaN-quieting instructions.
 DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-mllvm", "-amdgpu-mfma-vgpr-form"]
+          "-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]
 
 
 def hipcc() -> str:

@@ -52,6 +52,10 @@ constexpr int TILE_BYTES = KT * 256;     // one 128 x 128 bf16 tile (32 KB)
 constexpr int V_OFF = TILE_BYTES;        // V tile after K in a stage
 constexpr int STAGE = 2 * TILE_BYTES;    // bytes of LDS per pipeline stage (64 KB)
 constexpr float TAU = 8.0f;     // rescale O only when the running max grows by > 2^8
+// Start of the running max (log2 units): finite, below any real score, so a row that has
+// seen no admitted key gives exp2(-inf - m) = 0 and the first real block always rescales
+// (with alpha = exp2(m - mnew) = 0).
+constexpr float kMinRunningMax = -1.0e30f;
 
 // ---------------------------------------------------------------- layout helpers
 template <int MODE>
@@ -146,21 +150,22 @@ __device__ __forceinline__ int k8_swz(int row) { return (row >> 3) & 1; }
 // contiguous channels per lane, so the INT8 Q codes built from them line up with the
 // natural 16-byte chunks of the INT8 K rows.
 __device__ __forceinline__ int qk_chunk(int s, int lh) { return 4 * (s >> 1) + 2 * lh + (s & 1); }
-// Byte offset of the K fragment (key block kb of 32 rows, k-step s) for this lane.
+// Byte offset of the K fragment (key block kb of 32 rows, k-step s) for this lane.  Row
+// 32 kb + lq has the swizzle of lq (32 kb is a multiple of 16), so each offset is one of
+// two per-lane bases (by the parity of s) plus a compile-time constant: the fragment
+// reads then use the ds_read immediate offset.
+__device__ __forceinline__ int k_lane(int par, int lq, int lh) { return lq * 64 + (((2 * lh + par) ^ k_swz(lq)) << 4); }
 __device__ __forceinline__ int k_frag_off(int kb, int s, int lq, int lh) {
-  const int row = 32 * kb + lq;
-  return (s >> 1) * SLAB + row * 64 + (((2 * lh + (s & 1)) ^ k_swz(row)) << 4);
+  return k_lane(s & 1, lq, lh) + (s >> 1) * SLAB + kb * 2048;
 }
 // V^T tile in LDS: 4 slabs, one per 32-key sub-block, each [128 channel rows][64 B]: the
 // 16-byte chunk 2 k2 + lh of a row holds the 8 keys a P^T B-operand lane holds in k-step
-// k2 (keys 16 k2 + 8 (e / 4) + 4 lh + e % 4); swizzled like K.
+// k2 (keys 16 k2 + 8 (e / 4) + 4 lh + e % 4); swizzled like K (channel row 32 db + lq).
 __device__ __forceinline__ int vt_frag_off(int db, int kb, int k2, int lq, int lh) {
-  const int d = 32 * db + lq;
-  return kb * SLAB + d * 64 + (((2 * k2 + lh) ^ k_swz(d)) << 4);
+  return lq * 64 + (((2 * k2 + lh) ^ k_swz(lq)) << 4) + kb * SLAB + db * 2048;
 }
 __device__ __forceinline__ int k8_frag_off(int kb, int s, int lq, int lh) {
-  const int row = 32 * kb + lq;
-  return s * SLAB8 + row * 32 + ((lh ^ k8_swz(row)) << 4);
+  return lq * 32 + ((lh ^ k8_swz(lq)) << 4) + s * SLAB8 + kb * 1024;
 }
 
 __device__ __forceinline__ lds_void* as_lds(unsigned char* p) { return (lds_void*)p; }
@@ -442,15 +447,17 @@ __device__ __forceinline__ void sub_block(const AttnParams& p, const unsigned ch
     if (has_next2) dma_stage<MODE, NWAVE>(p, b, g, nxt2, (unsigned char*)buf, wave, lane);
   }
   __builtin_amdgcn_sched_barrier(0);
+  // region B holds the dependent Q K^T chain the next sub-block waits for: while it
+  // runs, this wave wins issue arbitration against its SIMD partner
+  __builtin_amdgcn_s_setprio(1);
   // ---- region B
   if (!LAST) Sn = qk_scores<BF16, MODE>(buf, cur.int8, kb + 1, lq, lh, qf, q8f);
   else if (has_next) Sn = qk_scores<BF16, MODE>(nbuf, nxt.int8, 0, lq, lh, qf, q8f);
-  const float muse = (ws.m == -INFINITY) ? 0.f : ws.m;
   if (PARTIAL) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) S[r] = __builtin_amdgcn_exp2f(S[r] - muse);
+    for (int r = 0; r < 16; ++r) S[r] = __builtin_amdgcn_exp2f(S[r] - ws.m);
   } else {
-    const float c = add - muse;
+    const float c = add - ws.m;
 #pragma unroll
     for (int r = 0; r < 16; ++r) S[r] = __builtin_amdgcn_exp2f(fmaf(S[r], mul, c));
   }
@@ -469,6 +476,7 @@ __device__ __forceinline__ void sub_block(const AttnParams& p, const unsigned ch
     ls = pair_sum<BF16>(pp.P[k2].w, ls);
   }
   ws.l = ls;
+  __builtin_amdgcn_s_setprio(0);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -558,7 +566,7 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) ws.O[db][r] = 0.f;
-  ws.m = -INFINITY;
+  ws.m = kMinRunningMax;
   ws.l = 0.f;
 
   if (nsteps > 0) {
