@@ -2,6 +2,7 @@
 // every argument are in include/krea_attn.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -176,6 +177,57 @@ krea::QuantParams make_quant(const attn_args& a, const attn_tensor* q, const att
   return qp;
 }
 
+// Compute units of the current device (cached per device id).
+int cu_count() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Tail split of one launch of `items` work items with `nb` key steps each.  With one
+// workgroup per compute unit, the items run in waves of `cus`; the `rem` items of the
+// last, partial wave each run as `split` workgroups over consecutive key ranges.  Their
+// rem * split parts take ceil(rem * split / cus) waves of 1 / split of an item plus a
+// fixed cost per part (pipeline fill, publishing and merging the partial state: about
+// 0.15 of a whole item as measured on the Krea shapes, where a split of 2 beat 8), and
+// the split is chosen to minimise that (ties: the smaller split).
+void plan_tail(krea::AttnParams& p, int64_t items, int nb, int cus, int capacity) {
+  p.n_full = (int)items;
+  p.split = 1;
+  static const int max_split = [] {
+    const char* e = std::getenv("KREA_ATTN_TAIL_SPLIT");  // cap on the split (0 or 1: off)
+    return e ? std::atoi(e) : krea::kMaxTailSplit;
+  }();
+  if (cus <= 0 || capacity < 2 || nb < 2 || max_split < 2) return;
+  const int64_t rem = items % cus;
+  if (rem == 0 || rem > krea::kMaxTailItems) return;
+  int best = 1;
+  double best_cost = 1.0;  // unsplit: one more wave of whole items
+  constexpr double kPartCost = 0.15;
+  for (int s = 2; s <= std::min({max_split, krea::kMaxTailSplit, nb}); ++s) {
+    if (rem * s > capacity) break;
+    const double cost = (double)((rem * s + cus - 1) / cus) * (1.0 / s + kPartCost);
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  if (best < 2) return;
+  p.n_full = (int)(items - rem);
+  p.split = best;
+  if (std::getenv("KREA_ATTN_LOG"))
+    std::fprintf(stderr, "[krea_attn] launch: %lld items on %d CUs, %d whole, %lld split in %d\n", (long long)items,
+                 cus, p.n_full, (long long)rem, best);
+}
+
 attn_status hip_check(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
   return ATTN_OK;
@@ -221,6 +273,10 @@ attn_status attn_forward(const attn_args* args, const attn_tensor* q, const attn
   p.o_sh = o->stride_h;
   const bool bf16 = a.dtype == ATTN_BF16;
   p.v_t = (const uint16_t*)((unsigned char*)workspace + w.v_t);
+  if (a.mode != ATTN_SCANLINE) {
+    p.tail_count = (int32_t*)((unsigned char*)workspace + w.tail_count);
+    p.tail_state = (float*)((unsigned char*)workspace + w.tail_state);
+  }
   if ((s = hip_check(krea::launch_v_relayout(p, (uint16_t*)p.v_t, a.mode, st), "V relayout launch")) != ATTN_OK)
     return s;
   if (a.mode == ATTN_TILEMIX) {
@@ -240,9 +296,11 @@ attn_status attn_forward(const attn_args* args, const attn_tensor* q, const attn
   const int chunk = a.q_chunk > 0 ? a.q_chunk : length;
   const int mode = a.mode;
   if (g_ev_start && (s = hip_check(hipEventRecord(g_ev_start, st), "timing event")) != ATTN_OK) return s;
+  const int cus = a.mode != ATTN_SCANLINE ? cu_count() : 0;
   for (int q0 = 0; q0 < length; q0 += chunk) {
     p.q_begin = q0;
     p.q_end = std::min(length, q0 + chunk);
+    plan_tail(p, krea::attention_items(a, p.q_end - p.q_begin), dp->plan.lay.nb, cus, w.tail_parts);
     if ((s = hip_check(krea::launch_attention(p, mode, bf16, st), "attention launch")) != ATTN_OK) return s;
   }
   if (g_ev_stop && (s = hip_check(hipEventRecord(g_ev_stop, st), "timing event")) != ATTN_OK) return s;

