@@ -273,11 +273,12 @@ attn_status attn_forward(const attn_args* args, const attn_tensor* q, const attn
   p.o_sh = o->stride_h;
   const bool bf16 = a.dtype == ATTN_BF16;
   p.v_t = (const uint16_t*)((unsigned char*)workspace + w.v_t);
+  p.k_norm = (float*)((unsigned char*)workspace + w.k_norm);
   if (a.mode != ATTN_SCANLINE) {
     p.tail_count = (int32_t*)((unsigned char*)workspace + w.tail_count);
     p.tail_state = (float*)((unsigned char*)workspace + w.tail_state);
   }
-  if ((s = hip_check(krea::launch_v_relayout(p, (uint16_t*)p.v_t, a.mode, st), "V relayout launch")) != ATTN_OK)
+  if ((s = hip_check(krea::launch_v_relayout(p, (uint16_t*)p.v_t, a.mode, bf16, st), "V relayout launch")) != ATTN_OK)
     return s;
   if (a.mode == ATTN_TILEMIX) {
     if (dp->plan.int8_tiles > 0) {

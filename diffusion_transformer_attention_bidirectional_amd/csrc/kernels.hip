@@ -56,6 +56,11 @@ constexpr float TAU = 8.0f;     // rescale O only when the running max grows by 
 // seen no admitted key gives exp2(-inf - m) = 0 and the first real block always rescales
 // (with alpha = exp2(m - mnew) = 0).
 constexpr float kMinRunningMax = -1.0e30f;
+// A step of full tiles skips the row max when no score in it can exceed the running max
+// by more than TAU_SKIP (log2 units): by Cauchy-Schwarz, scale * q . k <= scale |q| |k|,
+// and |k| is bounded per 128-key block by the relayout pass.  Then every probability is
+// at most 2^TAU_SKIP, far inside the range of the bf16 P and the fp32 sums.
+constexpr float TAU_SKIP = 24.0f;
 
 // ---------------------------------------------------------------- layout helpers
 template <int MODE>
@@ -423,8 +428,8 @@ __device__ __forceinline__ void sub_block(const AttnParams& p, const unsigned ch
                                           unsigned char* __restrict__ nbuf, const StepInfo& cur,
                                           const StepInfo& nxt, const StepInfo& nxt2, bool has_next, bool has_next2,
                                           int b, int g, int wave, int lane, int kb, float mul, float add,
-                                          const uint4 (&qf)[8], const uint4 (&q8f)[4], const QInfo& qinfo,
-                                          f32x16& S, f32x16& Sn, Pipe& pp, WaveState& ws) {
+                                          bool nomax, const uint4 (&qf)[8], const uint4 (&q8f)[4],
+                                          const QInfo& qinfo, f32x16& S, f32x16& Sn, Pipe& pp, WaveState& ws) {
   const int lq = lane & 31, lh = lane >> 5;
   // ---- region A
 #pragma unroll
@@ -435,32 +440,37 @@ __device__ __forceinline__ void sub_block(const AttnParams& p, const unsigned ch
   for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
     for (int db = 0; db < 4; ++db) pp.vf[k2][db] = *(const uint4*)(buf + V_OFF + vt_frag_off(db, kb, k2, lq, lh));
-  if (MODE == kModeTileMix && cur.int8) {
+  float alpha = 1.0f;
+  bool any_resc = false;
+  if (PARTIAL || !nomax) {  // wave-uniform: the row max, unless the step is known to be safe without it
+    if (MODE == kModeTileMix && cur.int8) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) S[r] = (float)__float_as_int(S[r]);
-  }
-  float mx;
-  if (PARTIAL) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int j = cur.k0 + 32 * kb + 8 * (r >> 2) + 4 * lh + (r & 3);
-      S[r] = admit<MODE>(p, qinfo, j) ? fmaf(S[r], mul, add) : -INFINITY;
+      for (int r = 0; r < 16; ++r) S[r] = (float)__float_as_int(S[r]);
     }
-    mx = S[0];
+    float mx;
+    if (PARTIAL) {
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-  } else {
-    float raw = S[0];
+      for (int r = 0; r < 16; ++r) {
+        const int j = cur.k0 + 32 * kb + 8 * (r >> 2) + 4 * lh + (r & 3);
+        S[r] = admit<MODE>(p, qinfo, j) ? fmaf(S[r], mul, add) : -INFINITY;
+      }
+      mx = S[0];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) raw = fmaxf(raw, S[r]);
-    mx = fmaf(raw, mul, add);
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+    } else {
+      float raw = S[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) raw = fmaxf(raw, S[r]);
+      mx = fmaf(raw, mul, add);
+    }
+    mx = pair_max(mx);
+    const float mnew = fmaxf(ws.m, mx);
+    const bool resc = mnew > ws.m + TAU;
+    alpha = resc ? __builtin_amdgcn_exp2f(ws.m - mnew) : 1.0f;
+    if (resc) ws.m = mnew;
+    any_resc = __any(resc);
   }
-  mx = pair_max(mx);
-  const float mnew = fmaxf(ws.m, mx);
-  const bool resc = mnew > ws.m + TAU;
-  const float alpha = resc ? __builtin_amdgcn_exp2f(ws.m - mnew) : 1.0f;
-  if (resc) ws.m = mnew;
-  if (__any(resc)) {
+  if (any_resc) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -518,18 +528,18 @@ __device__ __forceinline__ void attn_step(const AttnParams& p, const unsigned ch
                                           const StepInfo& nxt, const StepInfo& nxt2, bool has_next, bool has_next2,
                                           int b, int g, int wave, int lane, const uint4 (&qf)[8],
                                           const uint4 (&q8f)[4], const QInfo& qinfo, float qadd, float sq_l2,
-                                          f32x16& S0, f32x16& S1, Pipe& pp, WaveState& ws) {
+                                          bool nomax, f32x16& S0, f32x16& S1, Pipe& pp, WaveState& ws) {
   const bool int8 = MODE == kModeTileMix && cur.int8;
   const float mul = int8 ? sq_l2 * p.k_scale[((int64_t)b * p.heads_kv + g) * p.nb + (cur.k0 >> 7)] : p.scale_log2;
   const float add = int8 ? qadd : 0.f;
   sub_block<BF16, MODE, PARTIAL, false>(p, buf, nbuf, cur, nxt, nxt2, has_next, has_next2, b, g, wave, lane, 0, mul,
-                                        add, qf, q8f, qinfo, S0, S1, pp, ws);
+                                        add, nomax, qf, q8f, qinfo, S0, S1, pp, ws);
   sub_block<BF16, MODE, PARTIAL, false>(p, buf, nbuf, cur, nxt, nxt2, has_next, has_next2, b, g, wave, lane, 1, mul,
-                                        add, qf, q8f, qinfo, S1, S0, pp, ws);
+                                        add, nomax, qf, q8f, qinfo, S1, S0, pp, ws);
   sub_block<BF16, MODE, PARTIAL, false>(p, buf, nbuf, cur, nxt, nxt2, has_next, has_next2, b, g, wave, lane, 2, mul,
-                                        add, qf, q8f, qinfo, S0, S1, pp, ws);
+                                        add, nomax, qf, q8f, qinfo, S0, S1, pp, ws);
   sub_block<BF16, MODE, PARTIAL, true>(p, buf, nbuf, cur, nxt, nxt2, has_next, has_next2, b, g, wave, lane, 3, mul,
-                                       add, qf, q8f, qinfo, S1, S0, pp, ws);
+                                       add, nomax, qf, q8f, qinfo, S1, S0, pp, ws);
 }
 
 template <bool BF16, int MODE>
@@ -555,6 +565,23 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
   uint4 qf[8];
   load_q_frags<MODE>(p, b, h, tq, qf);
   const QInfo qinfo = query_info<MODE>(p, tq);
+  // scale_log2 |q| (rounded up): this lane holds half of its query's channels
+  float qn;
+  {
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const uint32_t w[4] = {qf[s].x, qf[s].y, qf[s].z, qf[s].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = elem_to_f32<BF16>(w[e] & 0xffff), x1 = elem_to_f32<BF16>(w[e] >> 16);
+        ss = fmaf(x0, x0, ss);
+        ss = fmaf(x1, x1, ss);
+      }
+    }
+    ss += __shfl_xor(ss, 32);
+    qn = __builtin_sqrtf(ss) * p.scale_log2 * 1.001f;
+  }
 
   // TileMix: INT8 codes of this query block, and the smooth_k row term.  Raw K is used on
   // FP16 tiles and mean-centred codes on INT8 tiles; adding scale * q . mean to every INT8
@@ -621,12 +648,15 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
     // rule) with the element mask: two loops, so the lean one keeps its registers
     const int nfull = MODE == kModeScan ? p.full_count[qa] : (p.n % KT ? nsteps - 1 : nsteps);
     const int f1 = min(s1, nfull);
+    const float* knorm = p.k_norm + ((int64_t)b * p.heads_kv + g) * p.nb;
     for (int i = s0; i < f1; ++i) {
       const bool has_next = i + 1 < s1, has_next2 = i + 2 < s1;
       const StepInfo nxt2 = has_next2 ? step_info<MODE>(p, qa, e0, i + 2) : nxt;
-      attn_step<BF16, MODE, false>(p, ((i - s0) & 1) ? st1 : st0, ((i - s0) & 1) ? st0 : st1, cur, nxt, nxt2,
-                                   has_next, has_next2, b, g, wave, lane, qf, q8f, qinfo, qadd, sq_l2, S0, S1, pp,
-                                   ws);
+      unsigned char* sa = ((i - s0) & 1) ? st1 : st0;
+      unsigned char* sb = ((i - s0) & 1) ? st0 : st1;
+      const bool nomax = !(MODE == kModeTileMix && cur.int8) && __all(qn * knorm[cur.k0 >> 7] <= ws.m + TAU_SKIP);
+      attn_step<BF16, MODE, false>(p, sa, sb, cur, nxt, nxt2, has_next, has_next2, b, g, wave, lane, qf, q8f, qinfo,
+                                   qadd, sq_l2, nomax, S0, S1, pp, ws);
       cur = nxt;
       nxt = nxt2;
     }
@@ -634,8 +664,8 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
       const bool has_next = i + 1 < s1, has_next2 = i + 2 < s1;
       const StepInfo nxt2 = has_next2 ? step_info<MODE>(p, qa, e0, i + 2) : nxt;
       attn_step<BF16, MODE, true>(p, ((i - s0) & 1) ? st1 : st0, ((i - s0) & 1) ? st0 : st1, cur, nxt, nxt2,
-                                  has_next, has_next2, b, g, wave, lane, qf, q8f, qinfo, qadd, sq_l2, S0, S1, pp,
-                                  ws);
+                                  has_next, has_next2, b, g, wave, lane, qf, q8f, qinfo, qadd, sq_l2, false, S0, S1,
+                                  pp, ws);
       cur = nxt;
       nxt = nxt2;
     }
@@ -714,13 +744,42 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
 // key order (scanline padding is zero), keys of each 16-key group in P^T order.  One
 // workgroup per (batch, KV head, 128-key block); the tile goes through LDS row-major and
 // comes back through transpose reads as exactly the fragments the attention kernel reads.
-template <int MODE>
+template <bool BF16, int MODE>
 __global__ void __launch_bounds__(256) v_relayout_kernel(const AttnParams p, uint16_t* v_t) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * SLAB];
   const int kb = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int lane = tid & 63, lq = lane & 31, lh = lane >> 5;
   // the attention launches that follow start from zero tail counters
   if (p.tail_count != nullptr && kb == 0 && g == 0 && b == 0) p.tail_count[tid] = 0;  // 256 counters
+  if (p.k_norm != nullptr) {
+    // largest |k| over the block's keys (two threads per key, 64 channels each), rounded up
+    __shared__ float kmax[4];
+    const int t = kb * KT + (tid >> 1);
+    float ss = 0.f;
+    if (tok_valid<MODE>(p, t)) {
+      const uint16_t* kr = (const uint16_t*)p.k.ptr + (int64_t)b * p.k.sb + (int64_t)g * p.k.sh +
+                           (int64_t)tok_phys<MODE>(p, t) * p.k.st + (tid & 1) * 64;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint4 x = *(const uint4*)(kr + 8 * c);
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x0 = elem_to_f32<BF16>(w[e] & 0xffff), x1 = elem_to_f32<BF16>(w[e] >> 16);
+          ss = fmaf(x0, x0, ss);
+          ss = fmaf(x1, x1, ss);
+        }
+      }
+    }
+    ss += __shfl_xor(ss, 1);
+#pragma unroll
+    for (int o = 32; o >= 2; o >>= 1) ss = fmaxf(ss, __shfl_xor(ss, o));
+    if (lane == 0) kmax[tid >> 6] = ss;
+    __syncthreads();
+    if (tid == 0)
+      p.k_norm[((int64_t)b * p.heads_kv + g) * p.nb + kb] =
+          __builtin_sqrtf(fmaxf(fmaxf(kmax[0], kmax[1]), fmaxf(kmax[2], kmax[3]))) * 1.001f;
+  }
   const uint16_t* vbase = (const uint16_t*)p.v.ptr + (int64_t)b * p.v.sb + (int64_t)g * p.v.sh;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -984,10 +1043,15 @@ hipError_t launch_attention(const AttnParams& p, int mode, bool bf16, hipStream_
   return hipGetLastError();
 }
 
-hipError_t launch_v_relayout(const AttnParams& p, uint16_t* v_t, int mode, hipStream_t s) {
+hipError_t launch_v_relayout(const AttnParams& p, uint16_t* v_t, int mode, bool bf16, hipStream_t s) {
   const dim3 grid(p.nb, p.heads_kv, p.batch);
-  if (mode == kModeScan) hipLaunchKernelGGL(v_relayout_kernel<kModeScan>, grid, dim3(256), 0, s, p, v_t);
-  else hipLaunchKernelGGL(v_relayout_kernel<kModeDense>, grid, dim3(256), 0, s, p, v_t);
+  if (bf16) {
+    if (mode == kModeScan) hipLaunchKernelGGL((v_relayout_kernel<true, kModeScan>), grid, dim3(256), 0, s, p, v_t);
+    else hipLaunchKernelGGL((v_relayout_kernel<true, kModeDense>), grid, dim3(256), 0, s, p, v_t);
+  } else {
+    if (mode == kModeScan) hipLaunchKernelGGL((v_relayout_kernel<false, kModeScan>), grid, dim3(256), 0, s, p, v_t);
+    else hipLaunchKernelGGL((v_relayout_kernel<false, kModeDense>), grid, dim3(256), 0, s, p, v_t);
+  }
   return hipGetLastError();
 }
 

@@ -41,6 +41,7 @@ struct AttnParams {
   const float* q_inv;      // [B, Hq, nb]
   const float* q_scale;    // [B, Hq, nb]
   const uint16_t* v_t;     // V^T tiles [B, Hkv, nb, 128 channels, 128 keys] (keys in P^T order)
+  float* k_norm;           // [B, Hkv, nb] upper bound of |k| over each 128-key block (relayout pass)
   // Tail split of this launch: items [0, n_full) run whole; each later item runs as
   // `split` workgroups over consecutive key ranges, merged through tail_count/tail_state.
   int n_full, split;
@@ -64,7 +65,7 @@ struct QuantParams {
 
 hipError_t launch_quant(const QuantParams& p, hipStream_t s);
 hipError_t launch_attention(const AttnParams& p, int mode, bool bf16, hipStream_t s);
-hipError_t launch_v_relayout(const AttnParams& p, uint16_t* v_t, int mode, hipStream_t s);
+hipError_t launch_v_relayout(const AttnParams& p, uint16_t* v_t, int mode, bool bf16, hipStream_t s);
 hipError_t launch_q_codes(const QuantParams& p, int8_t* q_codes, hipStream_t s);
 hipError_t launch_int8_scores(const AttnParams& p, const int32_t* tiles, int n_tiles, int32_t* out,
                               bool bf16, hipStream_t s);

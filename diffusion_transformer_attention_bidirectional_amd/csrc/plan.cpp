@@ -132,6 +132,7 @@ WorkspaceLayout workspace_layout(const attn_args& a) {
   const size_t bk = (size_t)a.batch * a.heads_kv, bq = (size_t)a.batch * a.heads_q;
   size_t off = 0;
   w.v_t = off;     off = align256(off + bk * l.nb * (size_t)kTile * kHeadDim * 2);
+  w.k_norm = off;  off = align256(off + bk * l.nb * sizeof(float));
   if (a.mode == ATTN_SCANLINE) {
     w.total = off;
     return w;

@@ -58,11 +58,12 @@ constexpr size_t kTailPartBytes = (size_t)kTailWaves * kTailFloats * 64 * sizeof
 int64_t attention_items(const attn_args& a, int q_tokens);
 
 // Offsets of the workspace regions (bytes, 256-aligned).  Every mode holds V^T tiles
-// [B, Hkv, nb, 128 channels, 128 keys]; dense and TileMix add the tail-split counters
+// [B, Hkv, nb, 128 channels, 128 keys] and the key-norm bounds; dense and TileMix add the tail-split counters
 // (int32 [kMaxTailItems]) and partial states (tail_parts x kTailPartBytes); TileMix adds
 // the quantiser state.
 struct WorkspaceLayout {
   size_t v_t = 0;
+  size_t k_norm = 0;  // fp32 [B, Hkv, nb]: largest key norm of each 128-key block
   size_t tail_count = 0, tail_state = 0;
   int tail_parts = 0;  // capacity of the partial-state region (0: never split)
   size_t k_part = 0, k_mean = 0, k_codes = 0, k_scale = 0, q_inv = 0, q_scale = 0;

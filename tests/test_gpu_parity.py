@@ -272,3 +272,19 @@ def test_kernel_events_hook(dev):
     assert 0.0 < span <= whole
     with pytest.raises(ka.KreaAttnError):
         ka.set_kernel_events(inner[0], None)
+
+
+@pytest.mark.parametrize("mode", ["dense", "tilemix"])
+def test_growing_key_norms(dev, mode):
+    """Keys whose norms grow block by block (and large queries): the bound that lets a step
+    skip the row max fails on later blocks, which must then rescale; results stay exact."""
+    w = _w(mode=mode, pattern="band", percentage=0.5, band_blocks=1, smooth_k=True, text_tokens=64, img_rows=20,
+           img_cols=32)
+    q, k, v = make_qkv(w)
+    n = w.tokens
+    grow = torch.tensor([1.0 + 0.75 * (t // 128) for t in range(n)], dtype=torch.float32).view(1, n, 1, 1)
+    k = (k.float() * grow).to(k.dtype)
+    q = (q.float() * 2.0).to(q.dtype)
+    got, _ = _run(w, dev, q, k, v)
+    ref = attn_ref.Oracle(to_f64(q), to_f64(k), to_f64(v), w).forward()
+    _assert_close(got, ref, f"growing norms {mode}")

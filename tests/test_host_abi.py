@@ -115,20 +115,26 @@ def test_block_mask_4mp_vs_oracle(lib):
 TAIL_PART_BYTES = 8 * 66 * 64 * 4  # 8 waves x (64 O values, max, sum) x 64 lanes, fp32
 
 
+def _a256(x):
+    return (x + 255) // 256 * 256
+
+
 def test_workspace_sizes(lib):
-    # every mode: V^T tiles, 12 KV heads x 36 blocks x 128 x 128 bf16
+    # every mode: V^T tiles (12 KV heads x 36 blocks x 128 x 128 bf16) and the fp32 key-norm
+    # bound of each 128-key block
     vt = 12 * 36 * 128 * 128 * 2
+    kn = _a256(12 * 36 * 4)
     # dense adds 256 tail counters and room for 256 partial states (864 items x 8 parts > 256)
     dense = ka.workspace_bytes(ka.make_args(text_tokens=512, img_rows=64, img_cols=64))
-    assert dense == vt + 256 * 4 + 256 * TAIL_PART_BYTES
+    assert dense == vt + kn + 256 * 4 + 256 * TAIL_PART_BYTES
     # a single 128-token block never splits: counters only
     one = ka.make_args(text_tokens=100, img_rows=0, img_cols=0, heads_q=4, heads_kv=1)
-    assert ka.workspace_bytes(one) == 128 * 128 * 2 + 1024
+    assert ka.workspace_bytes(one) == 128 * 128 * 2 + 256 + 1024
     # 2 blocks, 4 items (4 query tiles of 64 x 1 head group): room for items x min(nb, 8) parts
     two = ka.make_args(text_tokens=200, img_rows=0, img_cols=0, heads_q=4, heads_kv=1)
-    assert ka.workspace_bytes(two) == 2 * 128 * 128 * 2 + 1024 + 4 * 2 * TAIL_PART_BYTES
+    assert ka.workspace_bytes(two) == 2 * 128 * 128 * 2 + 256 + 1024 + 4 * 2 * TAIL_PART_BYTES
     scan = ka.make_args(text_tokens=77, img_rows=10, img_cols=12, heads_q=4, heads_kv=1, mode="scanline")
-    assert ka.workspace_bytes(scan) == 2 * 128 * 128 * 2  # padded logical length 256, never split
+    assert ka.workspace_bytes(scan) == 2 * 128 * 128 * 2 + 256  # padded logical length 256, never split
     tm = ka.make_args(text_tokens=512, img_rows=64, img_cols=64, mode="tilemix")
     n = ka.workspace_bytes(tm)
     # plus at least the INT8 K codes: 12 KV heads x 36 blocks x 128 x 128
