@@ -170,6 +170,7 @@ krea::QuantParams make_quant(const attn_args& a, const attn_tensor* q, const att
   qp.bf16 = a.dtype == ATTN_BF16;
   qp.k_part = (double*)(ws + w.k_part);
   qp.k_mean = (float*)(ws + w.k_mean);
+  qp.k_norm8 = (float*)(ws + w.k_norm8);
   qp.k_codes = (int8_t*)(ws + w.k_codes);
   qp.k_scale = (float*)(ws + w.k_scale);
   qp.q_inv = (float*)(ws + w.q_inv);
@@ -278,20 +279,22 @@ attn_status attn_forward(const attn_args* args, const attn_tensor* q, const attn
     p.tail_count = (int32_t*)((unsigned char*)workspace + w.tail_count);
     p.tail_state = (float*)((unsigned char*)workspace + w.tail_state);
   }
-  if ((s = hip_check(krea::launch_v_relayout(p, (uint16_t*)p.v_t, a.mode, bf16, st), "V relayout launch")) != ATTN_OK)
-    return s;
-  if (a.mode == ATTN_TILEMIX) {
-    if (dp->plan.int8_tiles > 0) {
-      const krea::QuantParams qp = make_quant(a, q, k, (unsigned char*)workspace);
-      if ((s = hip_check(krea::launch_quant(qp, st), "quantiser launch")) != ATTN_OK) return s;
-      p.k_mean = qp.k_mean;
-      p.k_codes = qp.k_codes;
-      p.k_scale = qp.k_scale;
-      p.q_inv = qp.q_inv;
-      p.q_scale = qp.q_scale;
-    } else {
-      p.route = nullptr;  // all FP16: the TileMix kernel never looks at INT8 state
-    }
+  if (a.mode == ATTN_TILEMIX && dp->plan.int8_tiles > 0) {
+    const krea::QuantParams qp = make_quant(a, q, k, (unsigned char*)workspace);
+    if ((s = hip_check(krea::launch_prepass(p, (uint16_t*)p.v_t, &qp, a.mode, bf16, st), "pre-pass launch")) != ATTN_OK)
+      return s;
+    if ((s = hip_check(krea::launch_quant_finish(qp, st), "quantiser launch")) != ATTN_OK) return s;
+    p.k_mean = qp.k_mean;
+    p.k_codes = qp.k_codes;
+    p.k_scale = qp.k_scale;
+    p.k_norm8 = qp.k_norm8;
+    p.q_inv = qp.q_inv;
+    p.q_scale = qp.q_scale;
+  } else {
+    if ((s = hip_check(krea::launch_prepass(p, (uint16_t*)p.v_t, nullptr, a.mode, bf16, st), "pre-pass launch")) !=
+        ATTN_OK)
+      return s;
+    if (a.mode == ATTN_TILEMIX) p.route = nullptr;  // all FP16: the TileMix kernel never looks at INT8 state
   }
   const int length = dp->plan.lay.length;
   const int chunk = a.q_chunk > 0 ? a.q_chunk : length;

@@ -28,6 +28,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstring>
 
 #include "kernels.hpp"
 
@@ -440,13 +441,13 @@ __device__ __forceinline__ void sub_block(const AttnParams& p, const unsigned ch
   for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
     for (int db = 0; db < 4; ++db) pp.vf[k2][db] = *(const uint4*)(buf + V_OFF + vt_frag_off(db, kb, k2, lq, lh));
+  if (MODE == kModeTileMix && cur.int8) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[r] = (float)__float_as_int(S[r]);
+  }
   float alpha = 1.0f;
   bool any_resc = false;
   if (PARTIAL || !nomax) {  // wave-uniform: the row max, unless the step is known to be safe without it
-    if (MODE == kModeTileMix && cur.int8) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) S[r] = (float)__float_as_int(S[r]);
-    }
     float mx;
     if (PARTIAL) {
 #pragma unroll
@@ -589,12 +590,27 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
   // for softmax, "The inputs that matter").
   uint4 q8f[4];
   float qadd = 0.f, sq_l2 = 0.f;
+  float qn8 = 0.f;  // sq_l2 |q8| (rounded up): the INT8 counterpart of qn
   if (MODE == kModeTileMix && p.q_inv != nullptr) {
     const int qidx = (b * p.heads_q + h) * p.nb + qa;
     const float inv = p.q_inv[qidx];
     sq_l2 = p.scale_log2 * p.q_scale[qidx];
 #pragma unroll
     for (int s = 0; s < 4; ++s) q8f[s] = make_q8<BF16>(qf[2 * s], qf[2 * s + 1], inv);
+    int ss = 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t w[4] = {q8f[s].x, q8f[s].y, q8f[s].z, q8f[s].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int c = (int)(int8_t)(w[e] >> (8 * k));
+          ss += c * c;
+        }
+    }
+    ss += __shfl_xor(ss, 32);
+    qn8 = __builtin_sqrtf((float)ss) * sq_l2 * 1.001f;
     if (p.smooth_k) {
       const float* mean = p.k_mean + ((int64_t)b * p.heads_kv + g) * 128;
       float acc = 0.f;
@@ -654,7 +670,14 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
       const StepInfo nxt2 = has_next2 ? step_info<MODE>(p, qa, e0, i + 2) : nxt;
       unsigned char* sa = ((i - s0) & 1) ? st1 : st0;
       unsigned char* sb = ((i - s0) & 1) ? st0 : st1;
-      const bool nomax = !(MODE == kModeTileMix && cur.int8) && __all(qn * knorm[cur.k0 >> 7] <= ws.m + TAU_SKIP);
+      bool nomax;
+      if (MODE == kModeTileMix && cur.int8) {
+        // |q8 . k8| <= |q8| |k8| (exact integers), so the score is at most this bound
+        const int64_t tile = ((int64_t)b * p.heads_kv + g) * p.nb + (cur.k0 >> 7);
+        nomax = __all(qn8 * p.k_norm8[tile] * p.k_scale[tile] + qadd <= ws.m + TAU_SKIP);
+      } else {
+        nomax = __all(qn * knorm[cur.k0 >> 7] <= ws.m + TAU_SKIP);
+      }
       attn_step<BF16, MODE, false>(p, sa, sb, cur, nxt, nxt2, has_next, has_next2, b, g, wave, lane, qf, q8f, qinfo,
                                    qadd, sq_l2, nomax, S0, S1, pp, ws);
       cur = nxt;
@@ -739,21 +762,44 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
   }
 }
 
-// ---------------------------------------------------------------- V^T relayout
-// Writes V^T tiles [B, Hkv, nb, 128 channels, 128 keys] for the attention kernel: logical
-// key order (scanline padding is zero), keys of each 16-key group in P^T order.  One
-// workgroup per (batch, KV head, 128-key block); the tile goes through LDS row-major and
-// comes back through transpose reads as exactly the fragments the attention kernel reads.
-template <bool BF16, int MODE>
-__global__ void __launch_bounds__(256) v_relayout_kernel(const AttnParams p, uint16_t* v_t) {
+// ---------------------------------------------------------------- per-block pre-pass
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+// max over the 256 threads of the block (every thread gets the result)
+__device__ __forceinline__ float block_max256(float x, float* red) {
+  x = wave_max(x);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  const float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return r;
+}
+
+// Everything the attention kernel needs from one 128-key block, in one pass over the
+// tensors.  One workgroup of 256 threads per (key block kb, KV head g, batch b):
+//   * V^T tiles [B, Hkv, nb, 128 channels, 128 keys] (when v_t is given): logical key order
+//     (scanline padding is zero), keys of each 16-key group in P^T order.  The tile goes
+//     through LDS row-major and comes back through transpose reads as exactly the
+//     fragments the attention kernel reads;
+//   * the bound on |k| over the block's keys (when p.k_norm is given);
+//   * QUANT, the TileMix quantiser inputs ("Krea 2 TileMix Attention (FP16/INT8 tiles)",
+//     "The inputs that matter"): the fp64 column sums of K over the block's tokens, added in
+//     token order (smooth_k), and the INT8 scale of query tile kb of every query head that
+//     KV head g serves (a = max |q| over the tile, inv = fp32(127 / a), scale = fp32(a / 127)).
+template <bool BF16, int MODE, bool QUANT>
+__global__ void __launch_bounds__(256) prepass_kernel(const AttnParams p, uint16_t* v_t, const QuantParams qp) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * SLAB];
+  __shared__ float kmax[4];
   const int kb = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const int lane = tid & 63, lq = lane & 31, lh = lane >> 5;
+  const int lane = tid & 63, lq = lane & 31, lh = lane >> 5, wave = tid >> 6;
+  const int64_t bg = (int64_t)b * p.heads_kv + g;
   // the attention launches that follow start from zero tail counters
   if (p.tail_count != nullptr && kb == 0 && g == 0 && b == 0) p.tail_count[tid] = 0;  // 256 counters
   if (p.k_norm != nullptr) {
     // largest |k| over the block's keys (two threads per key, 64 channels each), rounded up
-    __shared__ float kmax[4];
     const int t = kb * KT + (tid >> 1);
     float ss = 0.f;
     if (tok_valid<MODE>(p, t)) {
@@ -774,111 +820,117 @@ __global__ void __launch_bounds__(256) v_relayout_kernel(const AttnParams p, uin
     ss += __shfl_xor(ss, 1);
 #pragma unroll
     for (int o = 32; o >= 2; o >>= 1) ss = fmaxf(ss, __shfl_xor(ss, o));
-    if (lane == 0) kmax[tid >> 6] = ss;
+    if (lane == 0) kmax[wave] = ss;
     __syncthreads();
     if (tid == 0)
-      p.k_norm[((int64_t)b * p.heads_kv + g) * p.nb + kb] =
-          __builtin_sqrtf(fmaxf(fmaxf(kmax[0], kmax[1]), fmaxf(kmax[2], kmax[3]))) * 1.001f;
+      p.k_norm[bg * p.nb + kb] = __builtin_sqrtf(fmaxf(fmaxf(kmax[0], kmax[1]), fmaxf(kmax[2], kmax[3]))) * 1.001f;
   }
-  const uint16_t* vbase = (const uint16_t*)p.v.ptr + (int64_t)b * p.v.sb + (int64_t)g * p.v.sh;
+  if (v_t != nullptr) {
+    const uint16_t* vbase = (const uint16_t*)p.v.ptr + (int64_t)b * p.v.sb + (int64_t)g * p.v.sh;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int id = tid + 256 * i;
-    const int row = id >> 4, c = id & 15;
-    const int t = kb * KT + row;
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (tok_valid<MODE>(p, t)) x = *(const uint4*)(vbase + (int64_t)tok_phys<MODE>(p, t) * p.v.st + c * 8);
-    *(uint4*)(lds + (c >> 2) * SLAB + row * 64 + (c & 3) * 16) = x;
+    for (int i = 0; i < 8; ++i) {
+      const int id = tid + 256 * i;
+      const int row = id >> 4, c = id & 15;
+      const int t = kb * KT + row;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (tok_valid<MODE>(p, t)) x = *(const uint4*)(vbase + (int64_t)tok_phys<MODE>(p, t) * p.v.st + c * 8);
+      *(uint4*)(lds + (c >> 2) * SLAB + row * 64 + (c & 3) * 16) = x;
+    }
+    __syncthreads();
+    const int db = tid >> 6;
+    uint16_t* dst = v_t + ((bg * p.nb + kb) * 128 + 32 * db + lq) * 128;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 4; ++kb2)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+        *(uint4*)(dst + (4 * kb2 + 2 * k2 + lh) * 8) = v_frag(lds, db, kb2, k2, lane);
   }
-  __syncthreads();
-  const int db = tid >> 6;
-  uint16_t* dst = v_t + ((((int64_t)b * p.heads_kv + g) * p.nb + kb) * 128 + 32 * db + lq) * 128;
+  if (QUANT) {
+    // TileMix layouts are unpadded: token t of the block is row t of the tensors, valid
+    // when t < n
+    if (qp.smooth_k) {
+      // K tile rows into LDS ([128 tokens][256 B], zero rows past n), then one thread per
+      // channel adds the block's tokens in order
+      __syncthreads();  // the V^T transpose reads of the LDS are done
+      const uint16_t* kbase = (const uint16_t*)qp.k.ptr + (int64_t)b * qp.k.sb + (int64_t)g * qp.k.sh;
 #pragma unroll
-  for (int kb2 = 0; kb2 < 4; ++kb2)
+      for (int i = 0; i < 8; ++i) {
+        const int id = tid + 256 * i;
+        const int row = id >> 4, c = id & 15;
+        const int t = kb * KT + row;
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (t < qp.n) x = *(const uint4*)(kbase + (int64_t)t * qp.k.st + c * 8);
+        *(uint4*)(lds + row * 256 + c * 16) = x;
+      }
+      __syncthreads();
+      if (tid < 128) {
+        const int rows = min(KT, qp.n - kb * KT);
+        double acc = 0.0;
+#pragma unroll 16
+        for (int r = 0; r < rows; ++r)
+          acc = __dadd_rn(acc, (double)elem_to_f32<BF16>(*(const uint16_t*)(lds + r * 256 + tid * 2)));
+        qp.k_part[(bg * qp.nb + kb) * 128 + tid] = acc;
+      }
+    }
+    // Q tile scales: wave w takes the query heads w, w + 4, ... of this KV head
+    const int group = qp.heads_q / qp.heads_kv;
+    for (int hh = wave; hh < group; hh += 4) {
+      const int h = g * group + hh;
+      const uint16_t* src = (const uint16_t*)qp.q.ptr + (int64_t)b * qp.q.sb + (int64_t)h * qp.q.sh + (lane & 15) * 8;
+      float a = 0.f;
+#pragma unroll 8
+      for (int i = 0; i < 32; ++i) {
+        const int t = kb * KT + (lane >> 4) + 4 * i;
+        if (t < qp.n) {
+          const uint4 x = *(const uint4*)(src + (int64_t)t * qp.q.st);
+          const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
-      *(uint4*)(dst + (4 * kb2 + 2 * k2 + lh) * 8) = v_frag(lds, db, kb2, k2, lane);
+          for (int e = 0; e < 4; ++e) {
+            a = fmaxf(a, fabsf(elem_to_f32<BF16>(w[e] & 0xffff)));
+            a = fmaxf(a, fabsf(elem_to_f32<BF16>(w[e] >> 16)));
+          }
+        }
+      }
+      a = wave_max(a);
+      if (lane == 0) {
+        const int64_t idx = ((int64_t)b * qp.heads_q + h) * qp.nb + kb;
+        qp.q_inv[idx] = a > 0.f ? __fdiv_rn(127.0f, a) : 0.f;
+        qp.q_scale[idx] = a > 0.f ? __fdiv_rn(a, 127.0f) : 0.f;
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- quantiser
 // TileMix INT8 stage ("Krea 2 TileMix Attention (FP16/INT8 tiles)", "The inputs that
 // matter": smooth_k mean-centres K per head before quantisation).  Reproducible rule:
-// fp64 column sums of K, tokens of each 128-block added in order then the block sums in
-// order; m = fp32(sum / N); K_s = fp32(K) - m; per 128-token x 128-channel tile over
+// fp64 column sums of K, tokens of each 128-block added in order (pre-pass) then the block
+// sums in order; m = fp32(sum / N); K_s = fp32(K) - m; per 128-token x 128-channel tile over
 // valid rows a = max |x|, inv = fp32(127 / a), scale = fp32(a / 127),
 // code = clamp(rint(x * inv), -127, 127).
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-// max over the 256 threads of the block (every thread gets the result)
-__device__ __forceinline__ float block_max256(float x, float* red) {
-  x = wave_max(x);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  const float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  return r;
-}
-
-template <bool BF16>
-__global__ void __launch_bounds__(128) k_colsum_kernel(const QuantParams p) {
-  const int blk = blockIdx.x, g = blockIdx.y, b = blockIdx.z, c = threadIdx.x;
-  const uint16_t* src = (const uint16_t*)p.k.ptr + (int64_t)b * p.k.sb + (int64_t)g * p.k.sh + c;
-  const int t1 = min(p.n, blk * 128 + 128);
-  double acc = 0.0;
-  for (int t = blk * 128; t < t1; ++t) acc = __dadd_rn(acc, (double)elem_to_f32<BF16>(src[(int64_t)t * p.k.st]));
-  p.k_part[(((int64_t)b * p.heads_kv + g) * p.nb + blk) * 128 + c] = acc;
-}
-
-// Q tile scales: one workgroup per (batch, head, 128-token block).
-template <bool BF16>
-__global__ void __launch_bounds__(256) q_scale_kernel(const QuantParams p) {
-  __shared__ float red[4];
-  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const uint16_t* src = (const uint16_t*)p.q.ptr + (int64_t)b * p.q.sb + (int64_t)h * p.q.sh + (tid & 15) * 8;
-  float a = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int t = blk * 128 + (tid >> 4) + 16 * i;
-    if (t < p.n) {
-      const uint4 x = *(const uint4*)(src + (int64_t)t * p.q.st);
-      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        a = fmaxf(a, fabsf(elem_to_f32<BF16>(w[e] & 0xffff)));
-        a = fmaxf(a, fabsf(elem_to_f32<BF16>(w[e] >> 16)));
-      }
-    }
+// smooth_k mean per (batch, KV head, channel): one workgroup per (KV head, batch).
+__global__ void __launch_bounds__(128) k_mean_kernel(const QuantParams p) {
+  const int g = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+  const int64_t bg = (int64_t)b * p.heads_kv + g;
+  float m32 = 0.f;
+  if (p.smooth_k) {
+    double tot = 0.0;
+#pragma unroll 16
+    for (int j = 0; j < p.nb; ++j) tot = __dadd_rn(tot, p.k_part[(bg * p.nb + j) * 128 + c]);
+    m32 = __double2float_rn(__ddiv_rn(tot, (double)p.n));
   }
-  a = block_max256(a, red);
-  if (tid == 0) {
-    const int idx = ((int64_t)b * p.heads_q + h) * p.nb + blk;
-    p.q_inv[idx] = a > 0.f ? __fdiv_rn(127.0f, a) : 0.f;
-    p.q_scale[idx] = a > 0.f ? __fdiv_rn(a, 127.0f) : 0.f;
-  }
+  p.k_mean[bg * 128 + c] = m32;
 }
 
-// K codes: one workgroup per (batch, KV head, 128-token block).  Each workgroup first
-// finishes the smooth_k mean from the fp64 block sums (same order everywhere).
+// K codes: one workgroup per (batch, KV head, 128-token block), mean from k_mean_kernel.
 template <bool BF16>
 __global__ void __launch_bounds__(256) k_quant_kernel(const QuantParams p) {
   __shared__ float mean[128];
   __shared__ float red[4];
   const int blk = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int64_t bg = (int64_t)b * p.heads_kv + g;
-  if (tid < 128) {
-    float m32 = 0.f;
-    if (p.smooth_k) {
-      double tot = 0.0;
-      for (int j = 0; j < p.nb; ++j) tot = __dadd_rn(tot, p.k_part[(bg * p.nb + j) * 128 + tid]);
-      m32 = __double2float_rn(__ddiv_rn(tot, (double)p.n));
-    }
-    mean[tid] = m32;
-    if (blk == 0) p.k_mean[bg * 128 + tid] = m32;
-  }
+  if (tid < 128) mean[tid] = p.k_mean[bg * 128 + tid];
   __syncthreads();
   const int c8 = (tid & 15) * 8;
   const uint16_t* src = (const uint16_t*)p.k.ptr + (int64_t)b * p.k.sb + (int64_t)g * p.k.sh + c8;
@@ -901,17 +953,26 @@ __global__ void __launch_bounds__(256) k_quant_kernel(const QuantParams p) {
   const float inv = a > 0.f ? __fdiv_rn(127.0f, a) : 0.f;
   if (tid == 0) p.k_scale[bg * p.nb + blk] = a > 0.f ? __fdiv_rn(a, 127.0f) : 0.f;
   int8_t* dst = p.k_codes + ((bg * p.nb + blk) * 128) * 128 + c8;
+  int nmax = 0;  // largest squared norm of a code row (the 16 lanes of a row group share a row)
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = (tid >> 4) + 16 * i;
     uint32_t lo = 0, hi = 0;
+    int ss = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      lo |= (uint32_t)(quant8(x[i][e], inv) & 255) << (8 * e);
-      hi |= (uint32_t)(quant8(x[i][e + 4], inv) & 255) << (8 * e);
+      const int c0 = quant8(x[i][e], inv), c1 = quant8(x[i][e + 4], inv);
+      ss += c0 * c0 + c1 * c1;
+      lo |= (uint32_t)(c0 & 255) << (8 * e);
+      hi |= (uint32_t)(c1 & 255) << (8 * e);
     }
     *(uint2*)(dst + (int64_t)row * 128) = make_uint2(lo, hi);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o);
+    nmax = max(nmax, ss);
   }
+  const float n2 = block_max256((float)nmax, red);  // integers below 2^21: exact in fp32
+  if (tid == 0) p.k_norm8[bg * p.nb + blk] = __builtin_sqrtf(n2) * 1.001f;
 }
 
 // Q codes in natural layout [B, Hq, nb, 128, 128] with the attention kernel's quant8.
@@ -1000,18 +1061,36 @@ __global__ void __launch_bounds__(256) mask_counts_kernel(const AttnParams p, in
 }
 
 // ---------------------------------------------------------------- launchers
-hipError_t launch_quant(const QuantParams& p, hipStream_t s) {
-  const dim3 gk(p.nb, p.heads_kv, p.batch), gq(p.nb, p.heads_q, p.batch);
-  if (p.bf16) {
-    if (p.smooth_k) hipLaunchKernelGGL(k_colsum_kernel<true>, gk, dim3(128), 0, s, p);
-    hipLaunchKernelGGL(q_scale_kernel<true>, gq, dim3(256), 0, s, p);
-    hipLaunchKernelGGL(k_quant_kernel<true>, gk, dim3(256), 0, s, p);
-  } else {
-    if (p.smooth_k) hipLaunchKernelGGL(k_colsum_kernel<false>, gk, dim3(128), 0, s, p);
-    hipLaunchKernelGGL(q_scale_kernel<false>, gq, dim3(256), 0, s, p);
-    hipLaunchKernelGGL(k_quant_kernel<false>, gk, dim3(256), 0, s, p);
-  }
+hipError_t launch_quant_finish(const QuantParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(k_mean_kernel, dim3(p.heads_kv, p.batch), dim3(128), 0, s, p);
+  const dim3 gk(p.nb, p.heads_kv, p.batch);
+  if (p.bf16) hipLaunchKernelGGL(k_quant_kernel<true>, gk, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL(k_quant_kernel<false>, gk, dim3(256), 0, s, p);
   return hipGetLastError();
+}
+
+hipError_t launch_quant(const QuantParams& p, hipStream_t s) {
+  // the pre-pass without V^T, key norms or tail counters, over the unpadded layout
+  AttnParams a;
+  memset(&a, 0, sizeof(a));
+  a.q = p.q;
+  a.k = p.k;
+  a.batch = p.batch;
+  a.heads_q = p.heads_q;
+  a.heads_kv = p.heads_kv;
+  a.group = p.heads_q / p.heads_kv;
+  a.n = p.n;
+  a.text = p.text;
+  a.t_pad = p.text;
+  a.image = p.n - p.text;
+  a.cols = 1;
+  a.length = p.n;
+  a.nb = p.nb;
+  const dim3 gk(p.nb, p.heads_kv, p.batch);
+  if (p.bf16) hipLaunchKernelGGL((prepass_kernel<true, kModeTileMix, true>), gk, dim3(256), 0, s, a, nullptr, p);
+  else hipLaunchKernelGGL((prepass_kernel<false, kModeTileMix, true>), gk, dim3(256), 0, s, a, nullptr, p);
+  if (hipPeekAtLastError() != hipSuccess) return hipGetLastError();
+  return launch_quant_finish(p, s);
 }
 
 hipError_t launch_q_codes(const QuantParams& p, int8_t* q_codes, hipStream_t s) {
@@ -1043,14 +1122,20 @@ hipError_t launch_attention(const AttnParams& p, int mode, bool bf16, hipStream_
   return hipGetLastError();
 }
 
-hipError_t launch_v_relayout(const AttnParams& p, uint16_t* v_t, int mode, bool bf16, hipStream_t s) {
+hipError_t launch_prepass(const AttnParams& p, uint16_t* v_t, const QuantParams* qp, int mode, bool bf16,
+                          hipStream_t s) {
   const dim3 grid(p.nb, p.heads_kv, p.batch);
-  if (bf16) {
-    if (mode == kModeScan) hipLaunchKernelGGL((v_relayout_kernel<true, kModeScan>), grid, dim3(256), 0, s, p, v_t);
-    else hipLaunchKernelGGL((v_relayout_kernel<true, kModeDense>), grid, dim3(256), 0, s, p, v_t);
+  QuantParams none;
+  memset(&none, 0, sizeof(none));
+  if (qp != nullptr) {
+    if (bf16) hipLaunchKernelGGL((prepass_kernel<true, kModeTileMix, true>), grid, dim3(256), 0, s, p, v_t, *qp);
+    else hipLaunchKernelGGL((prepass_kernel<false, kModeTileMix, true>), grid, dim3(256), 0, s, p, v_t, *qp);
+  } else if (bf16) {
+    if (mode == kModeScan) hipLaunchKernelGGL((prepass_kernel<true, kModeScan, false>), grid, dim3(256), 0, s, p, v_t, none);
+    else hipLaunchKernelGGL((prepass_kernel<true, kModeDense, false>), grid, dim3(256), 0, s, p, v_t, none);
   } else {
-    if (mode == kModeScan) hipLaunchKernelGGL((v_relayout_kernel<false, kModeScan>), grid, dim3(256), 0, s, p, v_t);
-    else hipLaunchKernelGGL((v_relayout_kernel<false, kModeDense>), grid, dim3(256), 0, s, p, v_t);
+    if (mode == kModeScan) hipLaunchKernelGGL((prepass_kernel<false, kModeScan, false>), grid, dim3(256), 0, s, p, v_t, none);
+    else hipLaunchKernelGGL((prepass_kernel<false, kModeDense, false>), grid, dim3(256), 0, s, p, v_t, none);
   }
   return hipGetLastError();
 }

@@ -38,6 +38,7 @@ struct AttnParams {
   const float* k_mean;     // [B, Hkv, 128]
   const int8_t* k_codes;   // [B, Hkv, nb, 128, 128]
   const float* k_scale;    // [B, Hkv, nb]
+  const float* k_norm8;    // [B, Hkv, nb] upper bound of |k8| over each tile's code rows
   const float* q_inv;      // [B, Hq, nb]
   const float* q_scale;    // [B, Hq, nb]
   const uint16_t* v_t;     // V^T tiles [B, Hkv, nb, 128 channels, 128 keys] (keys in P^T order)
@@ -59,13 +60,20 @@ struct QuantParams {
   float* k_mean;      // [B, Hkv, 128]
   int8_t* k_codes;    // [B, Hkv, nb, 128, 128]
   float* k_scale;     // [B, Hkv, nb]
+  float* k_norm8;     // [B, Hkv, nb] largest code-row norm of each tile (rounded up)
   float* q_inv;       // [B, Hq, nb]
   float* q_scale;     // [B, Hq, nb]
 };
 
+// Quantiser for the debug exports: pre-pass (K column sums, Q scales), mean, K codes.
 hipError_t launch_quant(const QuantParams& p, hipStream_t s);
+// Mean and K codes after a pre-pass that computed the K column sums and Q scales.
+hipError_t launch_quant_finish(const QuantParams& p, hipStream_t s);
 hipError_t launch_attention(const AttnParams& p, int mode, bool bf16, hipStream_t s);
-hipError_t launch_v_relayout(const AttnParams& p, uint16_t* v_t, int mode, bool bf16, hipStream_t s);
+// Per-block pre-pass of attn_forward: V^T tiles, key-norm bounds, tail counters and, with
+// qp (TileMix), the K column sums and Q scales.
+hipError_t launch_prepass(const AttnParams& p, uint16_t* v_t, const QuantParams* qp, int mode, bool bf16,
+                          hipStream_t s);
 hipError_t launch_q_codes(const QuantParams& p, int8_t* q_codes, hipStream_t s);
 hipError_t launch_int8_scores(const AttnParams& p, const int32_t* tiles, int n_tiles, int32_t* out,
                               bool bf16, hipStream_t s);

@@ -151,6 +151,7 @@ WorkspaceLayout workspace_layout(const attn_args& a) {
   w.k_mean = off;  off = align256(off + bk * kHeadDim * sizeof(float));
   w.k_codes = off; off = align256(off + bk * l.nb * (size_t)kTile * kHeadDim);
   w.k_scale = off; off = align256(off + bk * l.nb * sizeof(float));
+  w.k_norm8 = off; off = align256(off + bk * l.nb * sizeof(float));
   w.q_inv = off;   off = align256(off + bq * l.nb * sizeof(float));
   w.q_scale = off; off = align256(off + bq * l.nb * sizeof(float));
   w.total = off;

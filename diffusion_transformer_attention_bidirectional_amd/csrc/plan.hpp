@@ -66,7 +66,7 @@ struct WorkspaceLayout {
   size_t k_norm = 0;  // fp32 [B, Hkv, nb]: largest key norm of each 128-key block
   size_t tail_count = 0, tail_state = 0;
   int tail_parts = 0;  // capacity of the partial-state region (0: never split)
-  size_t k_part = 0, k_mean = 0, k_codes = 0, k_scale = 0, q_inv = 0, q_scale = 0;
+  size_t k_part = 0, k_mean = 0, k_codes = 0, k_scale = 0, k_norm8 = 0, q_inv = 0, q_scale = 0;
   size_t total = 0;
 };
 
