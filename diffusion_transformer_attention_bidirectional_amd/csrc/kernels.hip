@@ -389,16 +389,24 @@ __device__ __forceinline__ float pair_sum(uint32_t pk, float acc) {
   }
 }
 
-// Raw scores S^T[key, q] of one 32-key sub-block: f32 on FP16 tiles, the int32
-// accumulators' bits on INT8 tiles (converted where the softmax reads them, so the
-// conversion never waits on the MFMA chain).
+// INT8 scores without an int -> float conversion: the int32 accumulation starts from the
+// bits of the MFMA inline constant 1 / (2 pi), 0x3E22F983, whose mantissa field
+// (2292099) leaves room for every q8 . k8 (|acc| <= 128 * 127^2 < 2^21) inside one binade.
+// Read as a float the result is exactly kInt8Base + acc * 2^-26, so the step's score
+// scale and offset absorb the affine map (mul * 2^26, add - kInt8Base * mul * 2^26).
+constexpr uint32_t kInt8BaseBits = 0x3E22F983u;
+constexpr float kInt8Base = __builtin_bit_cast(float, kInt8BaseBits);
+constexpr float kInt8Unit = 67108864.0f;  // 2^26
+
+// Raw scores S^T[key, q] of one 32-key sub-block: f32 on FP16 tiles; on INT8 tiles the
+// accumulator seeded as above, read as f32 (kInt8Base + acc * 2^-26).
 template <bool BF16, int MODE>
 __device__ __forceinline__ f32x16 qk_scores(const unsigned char* __restrict__ buf, bool int8, int kb, int lq, int lh,
                                             const uint4 (&qf)[8], const uint4 (&q8f)[4]) {
   if (MODE == kModeTileMix && int8) {
     i32x16 Si;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) Si[r] = 0;
+    for (int r = 0; r < 16; ++r) Si[r] = (int)kInt8BaseBits;
 #pragma unroll
     for (int s = 0; s < 4; ++s) Si = mma8(*(const uint4*)(buf + k8_frag_off(kb, s, lq, lh)), q8f[s], Si);
     return __builtin_bit_cast(f32x16, Si);
@@ -441,10 +449,6 @@ __device__ __forceinline__ void sub_block(const AttnParams& p, const unsigned ch
   for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
     for (int db = 0; db < 4; ++db) pp.vf[k2][db] = *(const uint4*)(buf + V_OFF + vt_frag_off(db, kb, k2, lq, lh));
-  if (MODE == kModeTileMix && cur.int8) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) S[r] = (float)__float_as_int(S[r]);
-  }
   float alpha = 1.0f;
   bool any_resc = false;
   if (PARTIAL || !nomax) {  // wave-uniform: the row max, unless the step is known to be safe without it
@@ -531,8 +535,11 @@ __device__ __forceinline__ void attn_step(const AttnParams& p, const unsigned ch
                                           const uint4 (&q8f)[4], const QInfo& qinfo, float qadd, float sq_l2,
                                           bool nomax, f32x16& S0, f32x16& S1, Pipe& pp, WaveState& ws) {
   const bool int8 = MODE == kModeTileMix && cur.int8;
-  const float mul = int8 ? sq_l2 * p.k_scale[((int64_t)b * p.heads_kv + g) * p.nb + (cur.k0 >> 7)] : p.scale_log2;
-  const float add = int8 ? qadd : 0.f;
+  // log2-domain score = S * mul + add (INT8: acc * sq_l2 * k_scale + qadd, through the seeded
+  // accumulator's affine map)
+  const float mul =
+      int8 ? sq_l2 * p.k_scale[((int64_t)b * p.heads_kv + g) * p.nb + (cur.k0 >> 7)] * kInt8Unit : p.scale_log2;
+  const float add = int8 ? qadd - kInt8Base * mul : 0.f;
   sub_block<BF16, MODE, PARTIAL, false>(p, buf, nbuf, cur, nxt, nxt2, has_next, has_next2, b, g, wave, lane, 0, mul,
                                         add, nomax, qf, q8f, qinfo, S0, S1, pp, ws);
   sub_block<BF16, MODE, PARTIAL, false>(p, buf, nbuf, cur, nxt, nxt2, has_next, has_next2, b, g, wave, lane, 1, mul,
