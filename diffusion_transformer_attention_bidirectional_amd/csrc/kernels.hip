@@ -355,6 +355,22 @@ __device__ __forceinline__ WorkItem work_item(const AttnParams& p, int n_qtiles,
   return w;
 }
 
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+// max over the 256 threads of the block (every thread gets the result)
+__device__ __forceinline__ float block_max256(float x, float* red) {
+  x = wave_max(x);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  const float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return r;
+}
+
 // ---------------------------------------------------------------- fused attention
 // Partial softmax states of split items: agent-scope (device-coherent) accesses.
 __device__ __forceinline__ void tail_store(float* p, float v) {
@@ -598,10 +614,42 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
   uint4 q8f[4];
   float qadd = 0.f, sq_l2 = 0.f;
   float qn8 = 0.f;  // sq_l2 |q8| (rounded up): the INT8 counterpart of qn
-  if (MODE == kModeTileMix && p.q_inv != nullptr) {
-    const int qidx = (b * p.heads_q + h) * p.nb + qa;
-    const float inv = p.q_inv[qidx];
-    sq_l2 = p.scale_log2 * p.q_scale[qidx];
+  if (MODE == kModeTileMix && p.route != nullptr) {
+    // INT8 scale of this query tile (the 128 tokens of head h in block qa), computed here:
+    // this wave's 32 queries are in registers, the 32 rows at the same place in the tile's
+    // other 64-token half are read, and the head's two waves combine through LDS
+    __shared__ float qabs[NWAVE];
+    float a = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const uint32_t w[4] = {qf[s].x, qf[s].y, qf[s].z, qf[s].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a = fmaxf(a, fabsf(elem_to_f32<BF16>(w[e] & 0xffff)));
+        a = fmaxf(a, fabsf(elem_to_f32<BF16>(w[e] >> 16)));
+      }
+    }
+    const int t_other = (q0 ^ 64) + 32 * (wave >> 2) + lq;
+    if (t_other < p.n) {
+      const uint16_t* src =
+          (const uint16_t*)p.q.ptr + (int64_t)b * p.q.sb + (int64_t)t_other * p.q.st + (int64_t)h * p.q.sh + 64 * lh;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint4 x = *(const uint4*)(src + 8 * c);
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a = fmaxf(a, fabsf(elem_to_f32<BF16>(w[e] & 0xffff)));
+          a = fmaxf(a, fabsf(elem_to_f32<BF16>(w[e] >> 16)));
+        }
+      }
+    }
+    a = wave_max(a);
+    if (lane == 0) qabs[wave] = a;
+    __syncthreads();
+    a = fmaxf(qabs[wave & 3], qabs[(wave & 3) + 4]);
+    const float inv = a > 0.f ? __fdiv_rn(127.0f, a) : 0.f;
+    sq_l2 = p.scale_log2 * (a > 0.f ? __fdiv_rn(a, 127.0f) : 0.f);
 #pragma unroll
     for (int s = 0; s < 4; ++s) q8f[s] = make_q8<BF16>(qf[2 * s], qf[2 * s + 1], inv);
     int ss = 0;
@@ -770,21 +818,6 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
 }
 
 // ---------------------------------------------------------------- per-block pre-pass
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-// max over the 256 threads of the block (every thread gets the result)
-__device__ __forceinline__ float block_max256(float x, float* red) {
-  x = wave_max(x);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  const float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  return r;
-}
-
 // Everything the attention kernel needs from one 128-key block, in one pass over the
 // tensors.  One workgroup of 256 threads per (key block kb, KV head g, batch b):
 //   * V^T tiles [B, Hkv, nb, 128 channels, 128 keys] (when v_t is given): logical key order
@@ -794,9 +827,10 @@ __device__ __forceinline__ float block_max256(float x, float* red) {
 //   * the bound on |k| over the block's keys (when p.k_norm is given);
 //   * QUANT, the TileMix quantiser inputs ("Krea 2 TileMix Attention (FP16/INT8 tiles)",
 //     "The inputs that matter"): the fp64 column sums of K over the block's tokens, added in
-//     token order (smooth_k), and the INT8 scale of query tile kb of every query head that
-//     KV head g serves (a = max |q| over the tile, inv = fp32(127 / a), scale = fp32(a / 127)).
-template <bool BF16, int MODE, bool QUANT>
+//     token order (smooth_k), and with QSCALE the INT8 scale of query tile kb of every query
+//     head that KV head g serves (a = max |q| over the tile, inv = fp32(127 / a),
+//     scale = fp32(a / 127)); the attention kernel derives the same scales itself.
+template <bool BF16, int MODE, bool QUANT, bool QSCALE>
 __global__ void __launch_bounds__(256) prepass_kernel(const AttnParams p, uint16_t* v_t, const QuantParams qp) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * SLAB];
   __shared__ float kmax[4];
@@ -879,8 +913,9 @@ __global__ void __launch_bounds__(256) prepass_kernel(const AttnParams p, uint16
         qp.k_part[(bg * qp.nb + kb) * 128 + tid] = acc;
       }
     }
-    // Q tile scales: wave w takes the query heads w, w + 4, ... of this KV head
-    const int group = qp.heads_q / qp.heads_kv;
+    // Q tile scales (the attention kernel computes its own): wave w takes the query heads
+    // w, w + 4, ... of this KV head
+    const int group = QSCALE ? qp.heads_q / qp.heads_kv : 0;
     for (int hh = wave; hh < group; hh += 4) {
       const int h = g * group + hh;
       const uint16_t* src = (const uint16_t*)qp.q.ptr + (int64_t)b * qp.q.sb + (int64_t)h * qp.q.sh + (lane & 15) * 8;
@@ -1094,8 +1129,8 @@ hipError_t launch_quant(const QuantParams& p, hipStream_t s) {
   a.length = p.n;
   a.nb = p.nb;
   const dim3 gk(p.nb, p.heads_kv, p.batch);
-  if (p.bf16) hipLaunchKernelGGL((prepass_kernel<true, kModeTileMix, true>), gk, dim3(256), 0, s, a, nullptr, p);
-  else hipLaunchKernelGGL((prepass_kernel<false, kModeTileMix, true>), gk, dim3(256), 0, s, a, nullptr, p);
+  if (p.bf16) hipLaunchKernelGGL((prepass_kernel<true, kModeTileMix, true, true>), gk, dim3(256), 0, s, a, nullptr, p);
+  else hipLaunchKernelGGL((prepass_kernel<false, kModeTileMix, true, true>), gk, dim3(256), 0, s, a, nullptr, p);
   if (hipPeekAtLastError() != hipSuccess) return hipGetLastError();
   return launch_quant_finish(p, s);
 }
@@ -1135,14 +1170,14 @@ hipError_t launch_prepass(const AttnParams& p, uint16_t* v_t, const QuantParams*
   QuantParams none;
   memset(&none, 0, sizeof(none));
   if (qp != nullptr) {
-    if (bf16) hipLaunchKernelGGL((prepass_kernel<true, kModeTileMix, true>), grid, dim3(256), 0, s, p, v_t, *qp);
-    else hipLaunchKernelGGL((prepass_kernel<false, kModeTileMix, true>), grid, dim3(256), 0, s, p, v_t, *qp);
+    if (bf16) hipLaunchKernelGGL((prepass_kernel<true, kModeTileMix, true, false>), grid, dim3(256), 0, s, p, v_t, *qp);
+    else hipLaunchKernelGGL((prepass_kernel<false, kModeTileMix, true, false>), grid, dim3(256), 0, s, p, v_t, *qp);
   } else if (bf16) {
-    if (mode == kModeScan) hipLaunchKernelGGL((prepass_kernel<true, kModeScan, false>), grid, dim3(256), 0, s, p, v_t, none);
-    else hipLaunchKernelGGL((prepass_kernel<true, kModeDense, false>), grid, dim3(256), 0, s, p, v_t, none);
+    if (mode == kModeScan) hipLaunchKernelGGL((prepass_kernel<true, kModeScan, false, false>), grid, dim3(256), 0, s, p, v_t, none);
+    else hipLaunchKernelGGL((prepass_kernel<true, kModeDense, false, false>), grid, dim3(256), 0, s, p, v_t, none);
   } else {
-    if (mode == kModeScan) hipLaunchKernelGGL((prepass_kernel<false, kModeScan, false>), grid, dim3(256), 0, s, p, v_t, none);
-    else hipLaunchKernelGGL((prepass_kernel<false, kModeDense, false>), grid, dim3(256), 0, s, p, v_t, none);
+    if (mode == kModeScan) hipLaunchKernelGGL((prepass_kernel<false, kModeScan, false, false>), grid, dim3(256), 0, s, p, v_t, none);
+    else hipLaunchKernelGGL((prepass_kernel<false, kModeDense, false, false>), grid, dim3(256), 0, s, p, v_t, none);
   }
   return hipGetLastError();
 }
