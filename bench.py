@@ -246,10 +246,17 @@ def main():
             if name == a.workload:
                 continue
             r = time_workload(name, max(5, a.steps // 2), max(2, a.warmup // 2), dev)
-            detail[name] = {k: r[k] for k in ("ms", "effective_tflops", "mfma_tflops", "roofline_frac",
-                                              "int8_tiles", "active_tiles", "plan_build_ms")}
-            print(f"# {name}: {r['ms']:.4f} ms/call, {r['effective_tflops']:.1f} eff TFLOP/s, "
-                  f"roofline {r['roofline_frac']:.3f}", file=sys.stderr, flush=True)
+            kms = attention_kernel_time(name, max(5, a.steps // 2), dev)
+            d = {k: r[k] for k in ("ms", "effective_tflops", "mfma_tflops", "roofline_frac", "int8_tiles",
+                                   "active_tiles", "plan_build_ms")}
+            # the attention launches alone, and what the rest of the call costs (pre-pass,
+            # quantiser, launch gaps)
+            d["attention_kernel_ms"] = kms
+            d["prework_ms"] = max(0.0, r["ms"] - kms)
+            d["kernel_roofline_frac"] = roofline_time_s(r["bf16_flops"], r["int8_ops"]) / (kms * 1e-3)
+            detail[name] = d
+            print(f"# {name}: {r['ms']:.4f} ms/call (attention {kms:.4f}), {r['effective_tflops']:.1f} eff "
+                  f"TFLOP/s, roofline {r['roofline_frac']:.3f}", file=sys.stderr, flush=True)
     cpu = None
     if not a.no_cpu:
         cpu = cpu_baseline(a.workload)
