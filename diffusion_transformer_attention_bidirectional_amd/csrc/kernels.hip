@@ -63,6 +63,20 @@ constexpr float kMinRunningMax = -1.0e30f;
 // at most 2^TAU_SKIP, far inside the range of the bf16 P and the fp32 sums.
 constexpr float TAU_SKIP = 24.0f;
 
+// Loads of values that stay fixed for a whole launch (plan arrays, the pre-pass and
+// quantiser outputs) at wave-uniform addresses, through the constant address space: they
+// become scalar loads, counted apart from the vector-memory counter that tracks the K/V
+// DMA, so waiting for one of them never waits for a tile in flight.
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) T*)p)[i];
+}
+__device__ __forceinline__ int ld_uniform_u8(const uint8_t* p, int64_t i) {
+  // bytes through the aligned dword that holds them
+  const uint32_t w = ld_uniform((const uint32_t*)((uintptr_t)(p + i) & ~(uintptr_t)3), 0);
+  return (int)((w >> (8 * ((uintptr_t)(p + i) & 3))) & 255);
+}
+
 // ---------------------------------------------------------------- layout helpers
 template <int MODE>
 __device__ __forceinline__ bool tok_valid(const AttnParams& p, int t) {
@@ -116,7 +130,7 @@ __device__ __forceinline__ StepInfo step_info(const AttnParams& p, int qa, int e
   StepInfo s;
   int kb;
   if (MODE == kModeScan) {
-    const int e = p.cols_list[e0 + i];
+    const int e = ld_uniform(p.cols_list, e0 + i);
     kb = e & 0xffff;
     s.partial = (e >> 16) != 0;
   } else {
@@ -124,14 +138,14 @@ __device__ __forceinline__ StepInfo step_info(const AttnParams& p, int qa, int e
   }
   s.k0 = kb * KT;
   if (MODE != kModeScan) s.partial = s.k0 + KT > p.n;
-  s.int8 = (MODE == kModeTileMix) && p.route != nullptr && p.route[qa * p.nb + kb] != 0;
+  s.int8 = (MODE == kModeTileMix) && p.route != nullptr && ld_uniform_u8(p.route, (int64_t)qa * p.nb + kb) != 0;
   return s;
 }
 template <int MODE>
 __device__ __forceinline__ int step_count(const AttnParams& p, int qa, int* e0) {
   if (MODE == kModeScan) {
-    *e0 = p.row_ptr[qa];
-    return p.row_ptr[qa + 1] - *e0;
+    *e0 = ld_uniform(p.row_ptr, qa);
+    return ld_uniform(p.row_ptr, qa + 1) - *e0;
   }
   *e0 = 0;
   return p.nb;
@@ -554,7 +568,8 @@ __device__ __forceinline__ void attn_step(const AttnParams& p, const unsigned ch
   // log2-domain score = S * mul + add (INT8: acc * sq_l2 * k_scale + qadd, through the seeded
   // accumulator's affine map)
   const float mul =
-      int8 ? sq_l2 * p.k_scale[((int64_t)b * p.heads_kv + g) * p.nb + (cur.k0 >> 7)] * kInt8Unit : p.scale_log2;
+      int8 ? sq_l2 * ld_uniform(p.k_scale, ((int64_t)b * p.heads_kv + g) * p.nb + (cur.k0 >> 7)) * kInt8Unit
+           : p.scale_log2;
   const float add = int8 ? qadd - kInt8Base * mul : 0.f;
   sub_block<BF16, MODE, PARTIAL, false>(p, buf, nbuf, cur, nxt, nxt2, has_next, has_next2, b, g, wave, lane, 0, mul,
                                         add, nomax, qf, q8f, qinfo, S0, S1, pp, ws);
@@ -717,7 +732,7 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
     f32x16 S0 = qk_scores<BF16, MODE>(st0, cur.int8, 0, lq, lh, qf, q8f), S1;
     // full tiles first, then the partial ones (padding, ragged tail, exact scanline
     // rule) with the element mask: two loops, so the lean one keeps its registers
-    const int nfull = MODE == kModeScan ? p.full_count[qa] : (p.n % KT ? nsteps - 1 : nsteps);
+    const int nfull = MODE == kModeScan ? ld_uniform(p.full_count, qa) : (p.n % KT ? nsteps - 1 : nsteps);
     const int f1 = min(s1, nfull);
     const float* knorm = p.k_norm + ((int64_t)b * p.heads_kv + g) * p.nb;
     for (int i = s0; i < f1; ++i) {
@@ -729,9 +744,9 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
       if (MODE == kModeTileMix && cur.int8) {
         // |q8 . k8| <= |q8| |k8| (exact integers), so the score is at most this bound
         const int64_t tile = ((int64_t)b * p.heads_kv + g) * p.nb + (cur.k0 >> 7);
-        nomax = __all(qn8 * p.k_norm8[tile] * p.k_scale[tile] + qadd <= ws.m + TAU_SKIP);
+        nomax = __all(qn8 * ld_uniform(p.k_norm8, tile) * ld_uniform(p.k_scale, tile) + qadd <= ws.m + TAU_SKIP);
       } else {
-        nomax = __all(qn * knorm[cur.k0 >> 7] <= ws.m + TAU_SKIP);
+        nomax = __all(qn * ld_uniform(knorm, cur.k0 >> 7) <= ws.m + TAU_SKIP);
       }
       attn_step<BF16, MODE, false>(p, sa, sb, cur, nxt, nxt2, has_next, has_next2, b, g, wave, lane, qf, q8f, qinfo,
                                    qadd, sq_l2, nomax, S0, S1, pp, ws);

@@ -78,6 +78,13 @@ SMALL = [
                          img_cols=40)),
     ("scan_textpad_tail", _w(mode="scanline", window=5, tile_aligned=True, text_tokens=200, img_rows=7,
                              img_cols=33)),
+    ("tilemix_b2_g8", _w(batch=2, heads_q=8, heads_kv=1, mode="tilemix", pattern="band", percentage=0.7,
+                         band_blocks=1, smooth_k=True, text_tokens=90, img_rows=10, img_cols=38)),
+    ("tilemix_band_all", _w(mode="tilemix", pattern="band", percentage=1.0, band_blocks=0, smooth_k=True,
+                            text_tokens=40, img_rows=16, img_cols=32)),
+    ("scan_f16_b2", _w(dtype="f16", batch=2, mode="scanline", window=5, tile_aligned=False, text_tokens=64,
+                       img_rows=9, img_cols=30)),
+    ("dense_scale", _w(softmax_scale=0.05, offset_std=0.0)),
 ]
 
 
@@ -217,7 +224,7 @@ def _sample_rows(n, t, rng, count=48):
     return np.array(sorted(r for r in rows if 0 <= r < n))
 
 
-@pytest.mark.parametrize("name", ["1mp_dense", "1mp_band", "1mp_scanline", "4mp_band"])
+@pytest.mark.parametrize("name", ["1mp_dense", "1mp_band", "1mp_scanline", "4mp_band", "4mp_dense"])
 def test_krea_shapes_sampled(dev, name):
     w = WORKLOADS[name]
     got, (q, k, v) = _run(w, dev)
