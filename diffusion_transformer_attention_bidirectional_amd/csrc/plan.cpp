@@ -76,8 +76,9 @@ attn_status validate_args(const attn_args& a, std::string& err) {
     return ATTN_ERR_INVALID_ARG;
   }
   if (a.mode == ATTN_TILEMIX) {
-    if (a.pattern != ATTN_PAT_ZERO && a.pattern != ATTN_PAT_ONE && a.pattern != ATTN_PAT_BAND) {
-      err = "pattern must be ATTN_PAT_ZERO, ATTN_PAT_ONE or ATTN_PAT_BAND";
+    if (a.pattern != ATTN_PAT_ZERO && a.pattern != ATTN_PAT_ONE && a.pattern != ATTN_PAT_BAND &&
+        a.pattern != ATTN_PAT_ALL) {
+      err = "pattern must be ATTN_PAT_ZERO, ATTN_PAT_ONE, ATTN_PAT_BAND or ATTN_PAT_ALL";
       return ATTN_ERR_INVALID_ARG;
     }
     if (!(a.percentage >= 0.0 && a.percentage <= 1.0)) {
@@ -173,7 +174,10 @@ std::vector<uint8_t> build_route_map(const attn_args& a, const Layout& lay, int6
   int64_t count = 0;
   // a block is a text block when it holds any text token
   const int first_image_block = blocks_of(lay.text);
-  if (a.pattern == ATTN_PAT_ONE) {
+  if (a.pattern == ATTN_PAT_ALL) {
+    std::fill(r.begin(), r.end(), 1);
+    count = (int64_t)nb * nb;
+  } else if (a.pattern == ATTN_PAT_ONE) {
     for (int qa = first_image_block; qa < nb; ++qa)
       for (int kb = first_image_block; kb < nb; ++kb) { r[(size_t)qa * nb + kb] = 1; ++count; }
   } else if (a.pattern == ATTN_PAT_BAND) {

@@ -63,7 +63,7 @@ enum {
 
 enum { ATTN_F16 = 0, ATTN_BF16 = 1, ATTN_F32 = 2 };
 enum { ATTN_DENSE = 0, ATTN_TILEMIX = 1, ATTN_SCANLINE = 2 };
-enum { ATTN_PAT_ZERO = 0, ATTN_PAT_ONE = 1, ATTN_PAT_BAND = 2 };
+enum { ATTN_PAT_ZERO = 0, ATTN_PAT_ONE = 1, ATTN_PAT_BAND = 2, ATTN_PAT_ALL = 3 };
 
 typedef struct {
   void* ptr;        /* device pointer to element [0, 0, 0, 0] */
@@ -85,7 +85,10 @@ typedef struct {
   int32_t mode;         /* ATTN_DENSE / ATTN_TILEMIX / ATTN_SCANLINE */
   /* TileMix ("Krea 2 TileMix Attention", "The inputs that matter") */
   int32_t pattern;      /* ATTN_PAT_ZERO (all FP16), ATTN_PAT_ONE (every image-image tile INT8),
-                           ATTN_PAT_BAND (diagonal band FP16, percentage of the rest INT8) */
+                           ATTN_PAT_BAND (diagonal band FP16, percentage of the rest INT8),
+                           ATTN_PAT_ALL (every tile INT8, text included: the comparison
+                           baseline of "What speedup to expect", a kernel that quantizes the
+                           text tiles too) */
   double percentage;    /* in [0, 1]: share of the image-image tiles outside the band sent to INT8;
                            count = floor(percentage * candidates) */
   int32_t band_blocks;  /* band half-width w >= 0 in 128-token blocks: |a - b| <= w stays FP16 */

@@ -60,11 +60,16 @@ def route_map(tokens: int, text_tokens: int, pattern: str, percentage: float = 0
               band_blocks: int = 2, seed: int = 0) -> np.ndarray:
     """uint8 [nb, nb] map over (query block a, key block b): 0 = FP16, 1 = INT8.
 
-    TileMix page, "What it actually patches" and "The inputs that matter".
+    TileMix page, "What it actually patches" and "The inputs that matter".  Pattern "all"
+    is the comparison baseline of the same page's "What speedup to expect": every tile
+    INT8, text tiles included, as in a kernel that quantizes the text tiles too.
     """
     nb = n_blocks(tokens)
     r = np.zeros((nb, nb), dtype=np.uint8)
     if pattern == "zero":
+        return r
+    if pattern == "all":
+        r[:, :] = 1
         return r
     image = [a for a in range(nb) if not is_text_block(a, text_tokens)]
     if pattern == "one":

@@ -87,6 +87,8 @@ WORKLOADS: Dict[str, Workload] = {
     # 4 MP dense on the same tensors (comparator for the band mode)
     "4mp_dense": Workload(name="4mp_dense", mode="dense", **_KREA_4MP),
     "4mp_dense_sliced": Workload(name="4mp_dense_sliced", mode="dense", q_chunk=4096, **_KREA_4MP),
+    # 4 MP scanline: 128x128 grid, one 128-token tile per grid row, window 11 (+-5 tiles)
+    "4mp_scanline": Workload(name="4mp_scanline", mode="scanline", window=11, tile_aligned=True, **_KREA_4MP),
 }
 
 _TORCH_DTYPE = {"bf16": torch.bfloat16, "f16": torch.float16}
@@ -124,3 +126,19 @@ def random_case(seed: int, batch: int, heads_q: int, heads_kv: int, head_dim: in
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact widening of a bf16/fp16 CPU tensor to a float64 numpy array."""
     return t.to(torch.float64).numpy()
+
+
+def text_outlier_case(w: Workload, text_scale: float = 4.0, outlier_channel: int = 7,
+                      outlier_value: float = 24.0):
+    """Q, K, V of workload ``w`` with the text tokens made adversarial for per-tile INT8:
+    text rows of Q and K scaled by ``text_scale`` and one K channel of every text token set
+    to ``outlier_value`` (text-encoder activations run larger than image ones and carry
+    outlier channels).  Returns CPU tensors in w.dtype."""
+    q, k, v = make_qkv(w)
+    t = w.text_tokens
+    qf, kf = q.float(), k.float()
+    qf[:, :t] *= text_scale
+    kf[:, :t] *= text_scale
+    kf[:, :t, :, outlier_channel] = outlier_value
+    dt = _TORCH_DTYPE[w.dtype]
+    return qf.to(dt), kf.to(dt), v

@@ -10,7 +10,7 @@ import torch
 
 import diffusion_transformer_attention_bidirectional_amd as ka
 from oracle import attn_ref, plan_ref, quant_ref
-from synth import WORKLOADS, Workload, make_qkv, to_f64
+from synth import WORKLOADS, Workload, make_qkv, text_outlier_case, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -85,6 +85,7 @@ SMALL = [
     ("scan_f16_b2", _w(dtype="f16", batch=2, mode="scanline", window=5, tile_aligned=False, text_tokens=64,
                        img_rows=9, img_cols=30)),
     ("dense_scale", _w(softmax_scale=0.05, offset_std=0.0)),
+    ("tilemix_all", _w(mode="tilemix", pattern="all", smooth_k=True, text_tokens=130, img_rows=12, img_cols=40)),
 ]
 
 
@@ -224,7 +225,7 @@ def _sample_rows(n, t, rng, count=48):
     return np.array(sorted(r for r in rows if 0 <= r < n))
 
 
-@pytest.mark.parametrize("name", ["1mp_dense", "1mp_band", "1mp_scanline", "4mp_band", "4mp_dense"])
+@pytest.mark.parametrize("name", ["1mp_dense", "1mp_band", "1mp_scanline", "4mp_band", "4mp_dense", "4mp_scanline"])
 def test_krea_shapes_sampled(dev, name):
     w = WORKLOADS[name]
     got, (q, k, v) = _run(w, dev)
@@ -295,3 +296,23 @@ def test_growing_key_norms(dev, mode):
     got, _ = _run(w, dev, q, k, v)
     ref = attn_ref.Oracle(to_f64(q), to_f64(k), to_f64(v), w).forward()
     _assert_close(got, ref, f"growing norms {mode}")
+
+
+def test_int8_baseline_on_text_outliers(dev):
+    """The kernel against the oracle in the TileMix band pattern and in the all-INT8
+    baseline, on inputs with large text tokens and an outlier K channel ("What speedup to
+    expect"): each matches the oracle of its own routing, and quantizing the text tiles
+    costs far more error against exact attention."""
+    w = _w(heads_q=4, heads_kv=1, mode="tilemix", pattern="band", percentage=0.5, band_blocks=1, smooth_k=True,
+           text_tokens=128, img_rows=16, img_cols=32, seed=21)
+    q, k, v = text_outlier_case(w)
+    qd, kd, vd = to_f64(q), to_f64(k), to_f64(v)
+    exact = attn_ref.attention(qd, kd, vd, w.with_(pattern="zero", smooth_k=False))
+    rel = {}
+    for pattern in ("band", "all"):
+        wp = w.with_(pattern=pattern)
+        got, _ = _run(wp, dev, q, k, v)
+        _assert_close(got, attn_ref.attention(qd, kd, vd, wp), f"{pattern} vs its oracle")
+        rel[pattern] = float(np.sqrt(np.mean((got - exact) ** 2) / np.mean(exact ** 2)))
+    print("rel RMS error against exact attention:", rel)
+    assert rel["all"] > 10.0 * rel["band"]

@@ -73,6 +73,8 @@ ROUTE_CASES = [
     (300, 0, "band", 0.9, 0, 2**63 + 5),
     (129, 1, "band", 1.0, 0, 3),
     (5000, 77, "band", 0.2, 3, 99),
+    (1500, 200, "all", 0.5, 2, 0),
+    (4608, 512, "all", 0.0, 0, 1),
 ]
 
 
@@ -110,6 +112,8 @@ def test_block_mask_bit_exact_vs_oracle(lib, t, rows, cols, window, aligned):
 def test_block_mask_4mp_vs_oracle(lib):
     args = ka.make_args(text_tokens=512, img_rows=128, img_cols=128, mode="scanline", window=11)
     assert (ka.block_mask(args) == plan_ref.block_mask(512, 128, 128, 11, True)).all()
+    info = ka.plan_info(args)
+    assert info["active_tiles"] == 2418 and info["partial_tiles"] == 0
 
 
 TAIL_PART_BYTES = 8 * 66 * 64 * 4  # 8 waves x (64 O values, max, sum) x 64 lanes, fp32

@@ -90,6 +90,8 @@ def test_route_patterns():
     band, left = _band_closed_form(nb - 2, 1)
     assert int(full.sum()) == left
     assert int(plan_ref.route_map(1500, 200, "band", 0.0, 1).sum()) == 0
+    # the comparison baseline quantizes every tile, text included
+    assert int(plan_ref.route_map(1500, 200, "all", 0.0, 5).sum()) == nb * nb
 
 
 def test_route_pick_is_smallest_keys_brute_force():
@@ -213,3 +215,19 @@ def test_layout_padding():
     phys = lay.physical(pos)
     assert sorted(phys[v].tolist()) == list(range(197))
     assert (phys[~v] == -1).all()
+
+
+def test_scanline_counts_closed_form_4mp():
+    # 512 text + 128x128 image: each 128-token image block is exactly one grid row, so image
+    # tiles (a, b) are active iff |a - b| <= window // 2; text rows and text keys are global
+    t, rows, cols, window = 512, 128, 128, 11
+    hw = window // 2
+    bm = plan_ref.block_mask(t, rows, cols, window, tile_aligned=True)
+    nb = bm.shape[0]
+    assert nb == 132
+    per_row = sum(min(rows - 1, r + hw) - max(0, r - hw) + 1 for r in range(rows))
+    assert per_row == 1378
+    assert int((bm != 0).sum()) == 4 * nb + rows * 4 + per_row == 2418
+    # whole rows per tile: the exact rule and tile_aligned admit the same pairs, all tiles full
+    assert set(np.unique(bm)) <= {0, 1}
+    assert (plan_ref.block_mask(t, rows, cols, window, tile_aligned=False) == bm).all()
