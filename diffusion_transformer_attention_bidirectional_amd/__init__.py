@@ -192,6 +192,40 @@ def plan_info(args: AttnArgs) -> dict:
     return {f: getattr(info, f) for f, _ in AttnPlanInfo._fields_}
 
 
+# ---------------------------------------------------------------- caller policy
+# The node wrappers on the pages decide whether their kernel runs at all: TileMix has an
+# `enabled` switch and leaves short sequences to the stock attention (`min_tokens`,
+# "Krea 2 TileMix Attention (FP16/INT8 tiles)", "The inputs that matter"), and prints one
+# line saying what is active.  The library itself has no fallback; these helpers give a
+# caller the same policy around it.
+
+def should_use(tokens: int, *, enabled: bool = True, min_tokens: int = 0) -> bool:
+    """True when a caller following the node's policy would run this library for a joint
+    sequence of `tokens` tokens (otherwise it keeps its own attention)."""
+    return bool(enabled) and tokens >= max(0, int(min_tokens))
+
+
+def describe(args: AttnArgs) -> str:
+    """One line naming the mode and what the plan routes or skips, for a caller's log."""
+    info = plan_info(args)
+    nb, total = info["n_blocks"], info["n_blocks"] ** 2
+    mode = {v: k for k, v in MODES.items()}.get(args.mode, str(args.mode))
+    head = (f"krea_attn {mode}: {args.heads_q} q / {args.heads_kv} kv heads, "
+            f"{info['logical_tokens']} tokens, {nb}x{nb} tiles")
+    if args.mode == MODES["tilemix"]:
+        pattern = {v: k for k, v in PATTERNS.items()}.get(args.pattern, str(args.pattern))
+        line = (f"{head}, pattern {pattern}: {info['int8_tiles']} INT8 "
+                f"({100.0 * info['int8_tiles'] / total:.1f} %), smooth_k {'on' if args.smooth_k else 'off'}")
+    elif args.mode == MODES["scanline"]:
+        line = (f"{head}, window {args.window}{' tile-aligned' if args.tile_aligned else ''}: "
+                f"{info['active_tiles']} active ({100.0 * info['active_tiles'] / total:.1f} %)")
+    else:
+        line = head
+    if args.q_chunk:
+        line += f", queries in slices of {args.q_chunk}"
+    return line
+
+
 def route_map(args: AttnArgs) -> np.ndarray:
     nb = plan_info(args)["n_blocks"]
     out = np.zeros((nb, nb), dtype=np.uint8)

@@ -236,3 +236,17 @@ def test_python_raises_loudly_without_library(tmp_path):
             ka.load_library(str(tmp_path / "nope.so"))
     finally:
         ka._lib = saved
+
+
+def test_caller_policy_helpers(lib):
+    assert ka.should_use(4608)
+    assert not ka.should_use(4608, enabled=False)
+    assert not ka.should_use(1000, min_tokens=1024) and ka.should_use(1024, min_tokens=1024)
+    band = ka.make_args(text_tokens=512, img_rows=64, img_cols=64, mode="tilemix", pattern="band",
+                        percentage=0.5, band_blocks=2)
+    assert ka.describe(band) == ("krea_attn tilemix: 48 q / 12 kv heads, 4608 tokens, 36x36 tiles, pattern band: "
+                                 "435 INT8 (33.6 %), smooth_k on")
+    scan = ka.make_args(text_tokens=512, img_rows=64, img_cols=64, mode="scanline", window=11, q_chunk=1024)
+    assert ka.describe(scan) == ("krea_attn scanline: 48 q / 12 kv heads, 4608 tokens, 36x36 tiles, window 11 "
+                                 "tile-aligned: 484 active (37.3 %), queries in slices of 1024")
+    assert ka.describe(ka.make_args(text_tokens=5)).startswith("krea_attn dense: 48 q / 12 kv heads, 5 tokens")
