@@ -5,7 +5,9 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-detail] [--no-cpu]
 One step = one attention call (attn_forward through the C ABI) on the 1 MP Krea 2 shape
 (B=1, 48 query / 12 KV heads, head_dim 128, 512 text + 64x64 image tokens, bf16, dense),
 inputs resident in HBM.  W untimed warm-up steps, then K timed steps bracketed by
-torch.cuda.synchronize(); one JSON line on stdout.
+torch.cuda.synchronize(); one JSON line on stdout.  The default W (200 calls, about 0.1 s
+at 1 MP) is sized so the timed steps see the GPU's steady state: the first few
+milliseconds of work after an idle period run up to ~10 % slower.
 
 value = effective TFLOP/s = 4 * Hq * N^2 * d / time per call (dense-equivalent flops).
 roofline: the attention kernel's algorithmic flops per launch / its mean launch duration
@@ -109,10 +111,44 @@ def time_workload(name, steps, warmup, dev):
     }
 
 
-def attention_kernel_time(name, steps, dev):
+class _HipRuntime:
+    """The HIP runtime already loaded in this process (torch's, which the library shares),
+    for timing events torch cannot create."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
+
+    def __init__(self):
+        import ctypes
+        import os
+
+        self.c = ctypes
+        self.lib = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD | os.RTLD_GLOBAL)
+
+    def event(self):
+        ev = self.c.c_void_p()
+        rc = self.lib.hipEventCreateWithFlags(self.c.byref(ev), self.c.c_uint(self.DISABLE_SYSTEM_FENCE))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        return ev
+
+    def elapsed_ms(self, a, b):
+        ms = self.c.c_float()
+        rc = self.lib.hipEventElapsedTime(self.c.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def destroy(self, ev):
+        self.lib.hipEventDestroy(ev)
+
+
+def attention_kernel_time(name, steps, warmup, dev):
     """Mean duration of the attention kernel alone: the library records a pair of HIP events
     on the call's stream just before the first and just after the last attention-kernel launch
-    of each call (the V relayout and the quantiser fall outside the span)."""
+    of each call (the V relayout and the quantiser fall outside the span).  The events are
+    created without the system-scope fence: with it, every stop event would wait for a
+    write-back of the L2 caches (tens of microseconds) that the back-to-back calls of the
+    throughput loop never pay, and the next launch would start on cold caches."""
     import torch
 
     import diffusion_transformer_attention_bidirectional_amd as ka
@@ -123,12 +159,10 @@ def attention_kernel_time(name, steps, dev):
     kw = workload_kwargs(w)
     out = torch.empty_like(q)
     ws = torch.empty(max(ka.workspace_bytes(ka.args_for(q, k, **kw)), 256), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    ka.attention(q, k, v, out=out, workspace=ws, **kw)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for a, b in evs:  # torch creates the HIP event on its first record
-        a.record(stream)
-        b.record(stream)
+    for _ in range(max(1, warmup)):
+        ka.attention(q, k, v, out=out, workspace=ws, **kw)
+    hip = _HipRuntime()
+    evs = [(hip.event(), hip.event()) for _ in range(steps)]
     torch.cuda.synchronize()
     try:
         for a, b in evs:
@@ -137,7 +171,11 @@ def attention_kernel_time(name, steps, dev):
     finally:
         ka.set_kernel_events()
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in evs) / steps
+    total = sum(hip.elapsed_ms(a, b) for a, b in evs)
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+    return total / steps
 
 
 def copy_reference(dev, nbytes=1 << 30, launches=5):
@@ -217,7 +255,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--workload", default=HEADLINE)
@@ -237,7 +275,7 @@ def main():
     head = time_workload(a.workload, a.steps, a.warmup, dev)
     print(f"# {a.workload}: {head['ms']:.4f} ms/call, {head['effective_tflops']:.1f} TFLOP/s", file=sys.stderr,
           flush=True)
-    kern_ms = attention_kernel_time(a.workload, a.steps, dev)
+    kern_ms = attention_kernel_time(a.workload, a.steps, a.warmup, dev)
     achieved = (head["bf16_flops"] + head["int8_ops"]) / (kern_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if head["int8_ops"] == 0 else roofline_peak_mixed(head["bf16_flops"], head["int8_ops"])
     detail = {}
@@ -246,7 +284,7 @@ def main():
             if name == a.workload:
                 continue
             r = time_workload(name, max(5, a.steps // 2), max(2, a.warmup // 2), dev)
-            kms = attention_kernel_time(name, max(5, a.steps // 2), dev)
+            kms = attention_kernel_time(name, max(5, a.steps // 2), max(2, a.warmup // 2), dev)
             d = {k: r[k] for k in ("ms", "effective_tflops", "mfma_tflops", "roofline_frac", "int8_tiles",
                                    "active_tiles", "plan_build_ms")}
             # the attention launches alone, and what the rest of the call costs (pre-pass,

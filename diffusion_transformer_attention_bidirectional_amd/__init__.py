@@ -177,11 +177,22 @@ def attention(q, k, v, *, text_tokens, img_rows=0, img_cols=0, mode="dense", out
 
 
 def set_kernel_events(start=None, stop=None):
-    """Record two recorded-once torch.cuda.Event objects around the attention-kernel
-    launches of every later attention() call on this thread; no arguments turns it off."""
+    """Record two events around the attention-kernel launches of every later attention()
+    call on this thread; no arguments turns it off.  Each is a torch.cuda.Event that has
+    been recorded once (torch creates the HIP event on its first record) or a raw hipEvent_t
+    handle (int or ctypes.c_void_p), e.g. one created with hipEventDisableSystemFence."""
     if (start is None) != (stop is None):
         raise KreaAttnError("give both events or neither")
-    ptr = (lambda e: None if e is None else ctypes.c_void_p(e.cuda_event))
+
+    def ptr(e):
+        if e is None:
+            return None
+        if isinstance(e, ctypes.c_void_p):
+            return e
+        if isinstance(e, int):
+            return ctypes.c_void_p(e)
+        return ctypes.c_void_p(e.cuda_event)
+
     _check(load_library().attn_set_kernel_events(ptr(start), ptr(stop)))
 
 

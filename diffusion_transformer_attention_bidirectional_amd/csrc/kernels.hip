@@ -195,13 +195,15 @@ __device__ __forceinline__ lds_void* as_lds(unsigned char* p) { return (lds_void
 // share the instructions.  K of a full tile is 128 consecutive tokens of the tensor, so
 // its addresses are one uniform base per step plus a per-lane 32-bit offset; a partial
 // tile clamps padding and out-of-range keys to row 0 (finite data; their probabilities
-// are zero).  V^T tiles are contiguous 32 KB blocks of the workspace.
-template <int MODE, int NW, bool WITH_V = true>
+// are zero).  V^T tiles are contiguous 32 KB blocks of the workspace.  PARTS selects the
+// K tile (or its INT8 codes) and / or the V^T tile.
+constexpr int kDmaK = 1, kDmaV = 2, kDmaAll = 3;
+template <int MODE, int NW, int PARTS = kDmaAll>
 __device__ __forceinline__ void dma_stage(const AttnParams& p, int b, int g, const StepInfo& s,
                                           unsigned char* stage, int wave, int lane) {
   constexpr int PER = (4 * SLAB / 1024) / NW;  // 1 KB blocks per wave per tile
   const int64_t bg = (int64_t)b * p.heads_kv + g;
-  if (!s.int8) {
+  if ((PARTS & 1) && !s.int8) {
     const char* kbase = (const char*)p.k.ptr + ((int64_t)b * p.k.sb + (int64_t)g * p.k.sh) * 2;
     if (!s.partial) {
       const char* kt = kbase + (int64_t)tok_phys<MODE>(p, s.k0) * p.k.st * 2;
@@ -224,7 +226,7 @@ __device__ __forceinline__ void dma_stage(const AttnParams& p, int b, int g, con
       }
     }
   }
-  if (WITH_V) {
+  if (PARTS & 2) {
     const char* vt = (const char*)p.v_t + ((bg * p.nb + (s.k0 >> 7)) << 15);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -234,7 +236,7 @@ __device__ __forceinline__ void dma_stage(const AttnParams& p, int b, int g, con
       __builtin_amdgcn_global_load_lds(vt + off, as_lds(stage + V_OFF + n * 1024), 16, 0, 0);
     }
   }
-  if (MODE == kModeTileMix && s.int8) {
+  if ((PARTS & 1) && MODE == kModeTileMix && s.int8) {
     constexpr int PER8 = (4 * SLAB8 / 1024) / NW;
     const int8_t* kc = p.k_codes + (bg * p.nb + (s.k0 >> 7)) * (128 * 128);
 #pragma unroll
@@ -430,10 +432,10 @@ constexpr float kInt8Unit = 67108864.0f;  // 2^26
 
 // Raw scores S^T[key, q] of one 32-key sub-block: f32 on FP16 tiles; on INT8 tiles the
 // accumulator seeded as above, read as f32 (kInt8Base + acc * 2^-26).
-template <bool BF16, int MODE>
-__device__ __forceinline__ f32x16 qk_scores(const unsigned char* __restrict__ buf, bool int8, int kb, int lq, int lh,
+template <bool BF16, bool INT8>
+__device__ __forceinline__ f32x16 qk_scores(const unsigned char* __restrict__ buf, int kb, int lq, int lh,
                                             const uint4 (&qf)[8], const uint4 (&q8f)[4]) {
-  if (MODE == kModeTileMix && int8) {
+  if (INT8) {
     i32x16 Si;
 #pragma unroll
     for (int r = 0; r < 16; ++r) Si[r] = (int)kInt8BaseBits;
@@ -448,26 +450,69 @@ __device__ __forceinline__ f32x16 qk_scores(const unsigned char* __restrict__ bu
   for (int s = 0; s < 8; ++s) S = mma16<BF16>(*(const uint4*)(buf + k_frag_off(kb, s, lq, lh)), qf[s], S);
   return S;
 }
+template <bool BF16, int MODE>
+__device__ __forceinline__ f32x16 qk_scores_any(const unsigned char* __restrict__ buf, bool int8, int kb, int lq,
+                                                int lh, const uint4 (&qf)[8], const uint4 (&q8f)[4]) {
+  if (MODE == kModeTileMix && int8) return qk_scores<BF16, true>(buf, kb, lq, lh, qf, q8f);
+  return qk_scores<BF16, false>(buf, kb, lq, lh, qf, q8f);
+}
 
 // Software pipeline over 32-key sub-blocks.  Sub-block j is handled in two scheduling
 // regions, so that every stretch of vector work has independent MFMAs beside it:
 //   A: O += V^T P^T of sub-block j - 1 (MFMA)   |  row max of S_j, lazy-rescale decision
 //   (rare branch: O *= alpha)
 //   B: S_{j+1} = K Q^T (MFMA)                   |  P_j = exp2(S_j), packing, row sums
-// At the last sub-block of a step the workgroup barrier (the next step's K/V^T tiles
-// have landed, this stage is free) sits between A and B, and the DMA of the step after
-// next is issued into the freed stage there.
+// The DMA of the next step's tiles into the other stage is issued in region A of the
+// first two sub-blocks (K or its INT8 codes, then V^T), so it neither arrives as one burst
+// nor sits on the barrier.  At the last sub-block the workgroup barrier sits between A and
+// B: every wave's share of the next step has landed, and every wave is done with this
+// stage, which receives the step after next while the next step runs.
 struct Pipe {
   uint4 P[2];      // P^T of the previous sub-block (two k-steps of 16 keys, packed)
   uint4 vf[2][4];  // V^T fragments of the previous sub-block
 };
 
+// P = exp2(S * mul + add - m) of one sub-block (S already masked and scaled on partial
+// tiles), packed as the P^T operand of the P V product, and the row sum of exactly those
+// rounded values.  The sum runs in two interleaved chains and is pinned to the calling
+// region: left alone, the compiler sinks the sums of all four sub-blocks into one
+// dependent chain at the end of the step.
+template <bool BF16, bool PARTIAL>
+__device__ __forceinline__ void probabilities(f32x16& S, float mul, float add, float alpha, Pipe& pp,
+                                              WaveState& ws) {
+  if (PARTIAL) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[r] = __builtin_amdgcn_exp2f(S[r] - ws.m);
+  } else {
+    const float c = add - ws.m;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[r] = __builtin_amdgcn_exp2f(fmaf(S[r], mul, c));
+  }
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+    const int r0 = 8 * k2;
+    pp.P[k2] = make_uint4(pack2<BF16>(S[r0], S[r0 + 1]), pack2<BF16>(S[r0 + 2], S[r0 + 3]),
+                          pack2<BF16>(S[r0 + 4], S[r0 + 5]), pack2<BF16>(S[r0 + 6], S[r0 + 7]));
+  }
+  float ls = ws.l * alpha, lb = 0.f;
+  ls = pair_sum<BF16>(pp.P[0].x, ls);
+  lb = pair_sum<BF16>(pp.P[1].x, lb);
+  ls = pair_sum<BF16>(pp.P[0].y, ls);
+  lb = pair_sum<BF16>(pp.P[1].y, lb);
+  ls = pair_sum<BF16>(pp.P[0].z, ls);
+  lb = pair_sum<BF16>(pp.P[1].z, lb);
+  ls = pair_sum<BF16>(pp.P[0].w, ls);
+  lb = pair_sum<BF16>(pp.P[1].w, lb);
+  ls += lb;
+  asm volatile("" : "+v"(ls));
+  ws.l = ls;
+}
+
 template <bool BF16, int MODE, bool PARTIAL, bool LAST>
 __device__ __forceinline__ void sub_block(const AttnParams& p, const unsigned char* __restrict__ buf,
-                                          unsigned char* __restrict__ nbuf, const StepInfo& cur,
-                                          const StepInfo& nxt, const StepInfo& nxt2, bool has_next, bool has_next2,
-                                          int b, int g, int wave, int lane, int kb, float mul, float add,
-                                          bool nomax, const uint4 (&qf)[8], const uint4 (&q8f)[4],
+                                          unsigned char* __restrict__ nbuf, int k0, bool int8, const StepInfo& nxt,
+                                          bool has_next, int b, int g, int wave, int lane, int kb, float mul,
+                                          float add, bool nomax, const uint4 (&qf)[8], const uint4 (&q8f)[4],
                                           const QInfo& qinfo, f32x16& S, f32x16& Sn, Pipe& pp, WaveState& ws) {
   const int lq = lane & 31, lh = lane >> 5;
   // ---- region A
@@ -479,6 +524,8 @@ __device__ __forceinline__ void sub_block(const AttnParams& p, const unsigned ch
   for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
     for (int db = 0; db < 4; ++db) pp.vf[k2][db] = *(const uint4*)(buf + V_OFF + vt_frag_off(db, kb, k2, lq, lh));
+  if (kb == 0 && has_next) dma_stage<MODE, NWAVE, kDmaK>(p, b, g, nxt, nbuf, wave, lane);
+  if (kb == 1 && has_next) dma_stage<MODE, NWAVE, kDmaV>(p, b, g, nxt, nbuf, wave, lane);
   float alpha = 1.0f;
   bool any_resc = false;
   if (PARTIAL || !nomax) {  // wave-uniform: the row max, unless the step is known to be safe without it
@@ -486,7 +533,7 @@ __device__ __forceinline__ void sub_block(const AttnParams& p, const unsigned ch
     if (PARTIAL) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int j = cur.k0 + 32 * kb + 8 * (r >> 2) + 4 * lh + (r & 3);
+        const int j = k0 + 32 * kb + 8 * (r >> 2) + 4 * lh + (r & 3);
         S[r] = admit<MODE>(p, qinfo, j) ? fmaf(S[r], mul, add) : -INFINITY;
       }
       mx = S[0];
@@ -512,58 +559,32 @@ __device__ __forceinline__ void sub_block(const AttnParams& p, const unsigned ch
       for (int r = 0; r < 16; ++r) ws.O[db][r] *= alpha;
   }
   if (LAST) {
-    // every wave is done with this stage (its V^T reads above, its K reads one sub-block
-    // ago) and its own DMA of the next step has landed: after the barrier the next
-    // step's tiles are complete and this stage can take the step after next
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (has_next2) dma_stage<MODE, NWAVE>(p, b, g, nxt2, (unsigned char*)buf, wave, lane);
   }
   __builtin_amdgcn_sched_barrier(0);
   // region B holds the dependent Q K^T chain the next sub-block waits for: while it
   // runs, this wave wins issue arbitration against its SIMD partner
   __builtin_amdgcn_s_setprio(1);
   // ---- region B
-  if (!LAST) Sn = qk_scores<BF16, MODE>(buf, cur.int8, kb + 1, lq, lh, qf, q8f);
-  else if (has_next) Sn = qk_scores<BF16, MODE>(nbuf, nxt.int8, 0, lq, lh, qf, q8f);
-  if (PARTIAL) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) S[r] = __builtin_amdgcn_exp2f(S[r] - ws.m);
-  } else {
-    const float c = add - ws.m;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) S[r] = __builtin_amdgcn_exp2f(fmaf(S[r], mul, c));
-  }
-#pragma unroll
-  for (int k2 = 0; k2 < 2; ++k2) {
-    const int r0 = 8 * k2;
-    pp.P[k2] = make_uint4(pack2<BF16>(S[r0], S[r0 + 1]), pack2<BF16>(S[r0 + 2], S[r0 + 3]),
-                          pack2<BF16>(S[r0 + 4], S[r0 + 5]), pack2<BF16>(S[r0 + 6], S[r0 + 7]));
-  }
-  float ls = ws.l * alpha;
-#pragma unroll
-  for (int k2 = 0; k2 < 2; ++k2) {
-    ls = pair_sum<BF16>(pp.P[k2].x, ls);
-    ls = pair_sum<BF16>(pp.P[k2].y, ls);
-    ls = pair_sum<BF16>(pp.P[k2].z, ls);
-    ls = pair_sum<BF16>(pp.P[k2].w, ls);
-  }
-  ws.l = ls;
+  if (!LAST) Sn = qk_scores_any<BF16, MODE>(buf, int8, kb + 1, lq, lh, qf, q8f);
+  else if (has_next) Sn = qk_scores_any<BF16, MODE>(nbuf, nxt.int8, 0, lq, lh, qf, q8f);
+  probabilities<BF16, PARTIAL>(S, mul, add, alpha, pp, ws);
   __builtin_amdgcn_s_setprio(0);
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// One step of 128 keys (four sub-blocks) on stage `buf`; the next step's tiles are in
-// `nbuf`.  On entry S0 holds the raw scores of this step's first sub-block; on exit it
-// holds those of the next step's first sub-block.  The two stages are separate
+// One step of 128 keys (four sub-blocks) on stage `buf`, while the next step's tiles are
+// loaded into `nbuf`.  On entry S0 holds the raw scores of this step's first sub-block; on
+// exit it holds those of the next step's first sub-block.  The two stages are separate
 // restrict-qualified pointers so the compiler knows the DMA cannot alias the reads.
 template <bool BF16, int MODE, bool PARTIAL>
 __device__ __forceinline__ void attn_step(const AttnParams& p, const unsigned char* __restrict__ buf,
                                           unsigned char* __restrict__ nbuf, const StepInfo& cur,
-                                          const StepInfo& nxt, const StepInfo& nxt2, bool has_next, bool has_next2,
-                                          int b, int g, int wave, int lane, const uint4 (&qf)[8],
-                                          const uint4 (&q8f)[4], const QInfo& qinfo, float qadd, float sq_l2,
-                                          bool nomax, f32x16& S0, f32x16& S1, Pipe& pp, WaveState& ws) {
+                                          const StepInfo& nxt, bool has_next, int b, int g, int wave, int lane,
+                                          const uint4 (&qf)[8], const uint4 (&q8f)[4], const QInfo& qinfo,
+                                          float qadd, float sq_l2, bool nomax, f32x16& S0, f32x16& S1, Pipe& pp,
+                                          WaveState& ws) {
   const bool int8 = MODE == kModeTileMix && cur.int8;
   // log2-domain score = S * mul + add (INT8: acc * sq_l2 * k_scale + qadd, through the seeded
   // accumulator's affine map)
@@ -571,14 +592,15 @@ __device__ __forceinline__ void attn_step(const AttnParams& p, const unsigned ch
       int8 ? sq_l2 * ld_uniform(p.k_scale, ((int64_t)b * p.heads_kv + g) * p.nb + (cur.k0 >> 7)) * kInt8Unit
            : p.scale_log2;
   const float add = int8 ? qadd - kInt8Base * mul : 0.f;
-  sub_block<BF16, MODE, PARTIAL, false>(p, buf, nbuf, cur, nxt, nxt2, has_next, has_next2, b, g, wave, lane, 0, mul,
-                                        add, nomax, qf, q8f, qinfo, S0, S1, pp, ws);
-  sub_block<BF16, MODE, PARTIAL, false>(p, buf, nbuf, cur, nxt, nxt2, has_next, has_next2, b, g, wave, lane, 1, mul,
-                                        add, nomax, qf, q8f, qinfo, S1, S0, pp, ws);
-  sub_block<BF16, MODE, PARTIAL, false>(p, buf, nbuf, cur, nxt, nxt2, has_next, has_next2, b, g, wave, lane, 2, mul,
-                                        add, nomax, qf, q8f, qinfo, S0, S1, pp, ws);
-  sub_block<BF16, MODE, PARTIAL, true>(p, buf, nbuf, cur, nxt, nxt2, has_next, has_next2, b, g, wave, lane, 3, mul,
-                                       add, nomax, qf, q8f, qinfo, S1, S0, pp, ws);
+  const int k0 = cur.k0;
+  sub_block<BF16, MODE, PARTIAL, false>(p, buf, nbuf, k0, int8, nxt, has_next, b, g, wave, lane, 0, mul, add, nomax,
+                                        qf, q8f, qinfo, S0, S1, pp, ws);
+  sub_block<BF16, MODE, PARTIAL, false>(p, buf, nbuf, k0, int8, nxt, has_next, b, g, wave, lane, 1, mul, add, nomax,
+                                        qf, q8f, qinfo, S1, S0, pp, ws);
+  sub_block<BF16, MODE, PARTIAL, false>(p, buf, nbuf, k0, int8, nxt, has_next, b, g, wave, lane, 2, mul, add, nomax,
+                                        qf, q8f, qinfo, S0, S1, pp, ws);
+  sub_block<BF16, MODE, PARTIAL, true>(p, buf, nbuf, k0, int8, nxt, has_next, b, g, wave, lane, 3, mul, add, nomax,
+                                       qf, q8f, qinfo, S1, S0, pp, ws);
 }
 
 template <bool BF16, int MODE>
@@ -719,7 +741,6 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
     StepInfo cur = step_info<MODE>(p, qa, e0, s0);
     StepInfo nxt = s0 + 1 < s1 ? step_info<MODE>(p, qa, e0, s0 + 1) : cur;
     dma_stage<MODE, NWAVE>(p, b, g, cur, st0, wave, lane);
-    if (s0 + 1 < s1) dma_stage<MODE, NWAVE>(p, b, g, nxt, st1, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     Pipe pp;
@@ -729,15 +750,15 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) pp.vf[k2][db] = make_uint4(0, 0, 0, 0);
     }
-    f32x16 S0 = qk_scores<BF16, MODE>(st0, cur.int8, 0, lq, lh, qf, q8f), S1;
+    f32x16 S0 = qk_scores_any<BF16, MODE>(st0, cur.int8, 0, lq, lh, qf, q8f), S1;
     // full tiles first, then the partial ones (padding, ragged tail, exact scanline
     // rule) with the element mask: two loops, so the lean one keeps its registers
     const int nfull = MODE == kModeScan ? ld_uniform(p.full_count, qa) : (p.n % KT ? nsteps - 1 : nsteps);
     const int f1 = min(s1, nfull);
     const float* knorm = p.k_norm + ((int64_t)b * p.heads_kv + g) * p.nb;
     for (int i = s0; i < f1; ++i) {
-      const bool has_next = i + 1 < s1, has_next2 = i + 2 < s1;
-      const StepInfo nxt2 = has_next2 ? step_info<MODE>(p, qa, e0, i + 2) : nxt;
+      const bool has_next = i + 1 < s1;
+      const StepInfo nxt2 = i + 2 < s1 ? step_info<MODE>(p, qa, e0, i + 2) : nxt;  // read a step ahead
       unsigned char* sa = ((i - s0) & 1) ? st1 : st0;
       unsigned char* sb = ((i - s0) & 1) ? st0 : st1;
       bool nomax;
@@ -748,17 +769,16 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
       } else {
         nomax = __all(qn * ld_uniform(knorm, cur.k0 >> 7) <= ws.m + TAU_SKIP);
       }
-      attn_step<BF16, MODE, false>(p, sa, sb, cur, nxt, nxt2, has_next, has_next2, b, g, wave, lane, qf, q8f, qinfo,
-                                   qadd, sq_l2, nomax, S0, S1, pp, ws);
+      attn_step<BF16, MODE, false>(p, sa, sb, cur, nxt, has_next, b, g, wave, lane, qf, q8f, qinfo, qadd, sq_l2,
+                                       nomax, S0, S1, pp, ws);
       cur = nxt;
       nxt = nxt2;
     }
     for (int i = max(s0, nfull); i < s1; ++i) {
-      const bool has_next = i + 1 < s1, has_next2 = i + 2 < s1;
-      const StepInfo nxt2 = has_next2 ? step_info<MODE>(p, qa, e0, i + 2) : nxt;
-      attn_step<BF16, MODE, true>(p, ((i - s0) & 1) ? st1 : st0, ((i - s0) & 1) ? st0 : st1, cur, nxt, nxt2,
-                                  has_next, has_next2, b, g, wave, lane, qf, q8f, qinfo, qadd, sq_l2, false, S0, S1,
-                                  pp, ws);
+      const bool has_next = i + 1 < s1;
+      const StepInfo nxt2 = i + 2 < s1 ? step_info<MODE>(p, qa, e0, i + 2) : nxt;  // read a step ahead
+      attn_step<BF16, MODE, true>(p, ((i - s0) & 1) ? st1 : st0, ((i - s0) & 1) ? st0 : st1, cur, nxt,
+                                      has_next, b, g, wave, lane, qf, q8f, qinfo, qadd, sq_l2, false, S0, S1, pp, ws);
       cur = nxt;
       nxt = nxt2;
     }
@@ -1074,7 +1094,7 @@ __global__ void __launch_bounds__(256) int8_scores_kernel(const AttnParams p, co
   si.k0 = kb * KT;
   si.partial = false;
   si.int8 = true;
-  dma_stage<kModeTileMix, 4, false>(p, b, g, si, lds, wave, lane);
+  dma_stage<kModeTileMix, 4, kDmaK>(p, b, g, si, lds, wave, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   int32_t* dst = out + (int64_t)blockIdx.x * 128 * 128;
