@@ -29,7 +29,7 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported dtype", -3: "unsuppo
           -4: "workspace too small", -5: "device error"}
 
 EXPORTS = ("attn_workspace_bytes", "attn_forward", "attn_plan_info_get", "attn_route_map",
-           "attn_block_mask", "attn_quantize", "attn_int8_scores", "attn_mask_row_counts",
+           "attn_block_mask", "attn_item_order", "attn_quantize", "attn_int8_scores", "attn_mask_row_counts",
            "attn_set_kernel_events", "attn_status_string", "attn_last_error")
 
 
@@ -85,6 +85,7 @@ def load_library(path: str = LIB_PATH):
         "attn_plan_info_get": [P(AttnArgs), P(AttnPlanInfo)],
         "attn_route_map": [P(AttnArgs), vp, i32],
         "attn_block_mask": [P(AttnArgs), vp, i32],
+        "attn_item_order": [P(AttnArgs), i32, vp, ctypes.c_int64],
         "attn_quantize": [P(AttnArgs), P(AttnTensor), P(AttnTensor), vp, sz, vp, vp, vp, vp, vp, vp],
         "attn_int8_scores": [P(AttnArgs), P(AttnTensor), P(AttnTensor), vp, sz, vp, i32, vp, vp],
         "attn_mask_row_counts": [P(AttnArgs), vp, vp],
@@ -249,6 +250,18 @@ def block_mask(args: AttnArgs) -> np.ndarray:
     out = np.zeros((nb, nb), dtype=np.uint8)
     _check(load_library().attn_block_mask(ctypes.byref(args), out.ctypes.data, nb))
     return out
+
+
+def item_order(args: AttnArgs, slice_index: int = 0) -> np.ndarray:
+    """Scanline: the work item each workgroup of one query slice's launch runs."""
+    info = plan_info(args)
+    rows = info["logical_tokens"]
+    chunk = args.q_chunk if args.q_chunk > 0 else rows
+    lo = slice_index * chunk
+    n = ((min(rows, lo + chunk) - lo + 63) // 64) * (args.heads_q // 4) * args.batch if lo < rows else 0
+    out = np.zeros(max(n, 1), dtype=np.int32)
+    _check(load_library().attn_item_order(ctypes.byref(args), int(slice_index), out.ctypes.data, int(n)))
+    return out[:n]
 
 
 # ---------------------------------------------------------------- device debug views

@@ -28,13 +28,14 @@ attn_status fail(attn_status s, const std::string& msg) {
 }
 
 // A plan plus its device copy.  Device layout: route map [nb * nb] (TileMix) or
-// row_ptr [nb + 1] int32 then cols [nnz] int32 (scanline).
+// row_ptr [nb + 1] int32, cols [nnz] int32, full_count [nb] int32 and the workgroup
+// order of every slice (scanline).
 struct DevicePlan {
   std::string key;
   int device = -1;
   krea::Plan plan;
   unsigned char* dmem = nullptr;
-  size_t route_off = 0, row_ptr_off = 0, cols_off = 0, full_off = 0;
+  size_t route_off = 0, row_ptr_off = 0, cols_off = 0, full_off = 0, order_off = 0;
   ~DevicePlan() {
     if (dmem) {
       int cur = 0;
@@ -76,6 +77,8 @@ attn_status get_plan(const attn_args& a, std::shared_ptr<DevicePlan>* out) {
   bytes += (p.cols.size() * 4 + 255) & ~(size_t)255;
   dp->full_off = bytes;
   bytes += (p.full_count.size() * 4 + 255) & ~(size_t)255;
+  dp->order_off = bytes;
+  bytes += (p.item_order.size() * 4 + 255) & ~(size_t)255;
   if (bytes == 0) bytes = 256;
   if (hipMalloc((void**)&dp->dmem, bytes) != hipSuccess) {
     dp->dmem = nullptr;
@@ -89,6 +92,8 @@ attn_status get_plan(const attn_args& a, std::shared_ptr<DevicePlan>* out) {
     e = hipMemcpy(dp->dmem + dp->cols_off, p.cols.data(), p.cols.size() * 4, hipMemcpyHostToDevice);
   if (e == hipSuccess && !p.full_count.empty())
     e = hipMemcpy(dp->dmem + dp->full_off, p.full_count.data(), p.full_count.size() * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess && !p.item_order.empty())
+    e = hipMemcpy(dp->dmem + dp->order_off, p.item_order.data(), p.item_order.size() * 4, hipMemcpyHostToDevice);
   if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, std::string("plan upload failed: ") + hipGetErrorString(e));
   if (std::getenv("KREA_ATTN_LOG")) {
     std::fprintf(stderr, "[krea_attn] plan built: mode %d, %d blocks, %lld INT8 tiles, %lld active, %lld partial\n",
@@ -301,10 +306,12 @@ attn_status attn_forward(const attn_args* args, const attn_tensor* q, const attn
   const int mode = a.mode;
   if (g_ev_start && (s = hip_check(hipEventRecord(g_ev_start, st), "timing event")) != ATTN_OK) return s;
   const int cus = a.mode != ATTN_SCANLINE ? cu_count() : 0;
-  for (int q0 = 0; q0 < length; q0 += chunk) {
+  for (int q0 = 0, slice = 0; q0 < length; q0 += chunk, ++slice) {
     p.q_begin = q0;
     p.q_end = std::min(length, q0 + chunk);
     plan_tail(p, krea::attention_items(a, p.q_end - p.q_begin), dp->plan.lay.nb, cus, w.tail_parts);
+    if (!dp->plan.item_order.empty())
+      p.item_order = (const int32_t*)(dp->dmem + dp->order_off) + dp->plan.slice_begin[slice];
     if ((s = hip_check(krea::launch_attention(p, mode, bf16, st), "attention launch")) != ATTN_OK) return s;
   }
   if (g_ev_stop && (s = hip_check(hipEventRecord(g_ev_stop, st), "timing event")) != ATTN_OK) return s;
@@ -348,6 +355,20 @@ attn_status attn_block_mask(const attn_args* args, uint8_t* out, int32_t nb) {
   if (!out || nb != l.nb) return fail(ATTN_ERR_INVALID_ARG, "out is NULL or nb does not match the plan");
   const std::vector<uint8_t> m = krea::build_block_mask(*args, l);
   std::memcpy(out, m.data(), m.size());
+  g_err.clear();
+  return ATTN_OK;
+}
+
+attn_status attn_item_order(const attn_args* args, int32_t slice, int32_t* out, int64_t n) {
+  attn_status s = check_args(args);
+  if (s != ATTN_OK) return s;
+  if (args->mode != ATTN_SCANLINE) return fail(ATTN_ERR_INVALID_ARG, "item order exists for ATTN_SCANLINE only");
+  const krea::Plan p = krea::build_plan(*args);
+  if (slice < 0 || slice >= (int32_t)p.slice_begin.size()) return fail(ATTN_ERR_INVALID_ARG, "slice out of range");
+  const size_t b = (size_t)p.slice_begin[slice];
+  const size_t e = slice + 1 < (int32_t)p.slice_begin.size() ? (size_t)p.slice_begin[slice + 1] : p.item_order.size();
+  if (!out || n != (int64_t)(e - b)) return fail(ATTN_ERR_INVALID_ARG, "out is NULL or n is not the launch's size");
+  std::memcpy(out, p.item_order.data() + b, (e - b) * sizeof(int32_t));
   g_err.clear();
   return ATTN_OK;
 }

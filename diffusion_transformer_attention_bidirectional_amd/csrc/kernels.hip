@@ -350,10 +350,14 @@ __device__ __forceinline__ WorkItem work_item(const AttnParams& p, int n_qtiles,
   const int L = blockIdx.x;
   int item;
   if (L < p.n_full) {
-    const int total = p.n_full;
-    const int xcd = L & 7, idx = L >> 3;
-    const int per = total >> 3, rem = total & 7;
-    item = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    if (p.item_order != nullptr) {
+      item = ld_uniform(p.item_order, L);  // the same XCD ranges, longest items first
+    } else {
+      const int total = p.n_full;
+      const int xcd = L & 7, idx = L >> 3;
+      const int per = total >> 3, rem = total & 7;
+      item = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    }
     w.part = 0;
     w.nparts = 1;
     w.slot = -1;

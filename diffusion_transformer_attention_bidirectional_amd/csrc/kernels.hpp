@@ -35,6 +35,7 @@ struct AttnParams {
   const int32_t* row_ptr;  // scanline tile lists
   const int32_t* cols_list;
   const int32_t* full_count;  // scanline: full tiles at the head of each list
+  const int32_t* item_order;  // scanline: work item of each workgroup of this launch
   const float* k_mean;     // [B, Hkv, 128]
   const int8_t* k_codes;   // [B, Hkv, nb, 128, 128]
   const float* k_scale;    // [B, Hkv, nb]

@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstring>
 #include <tuple>
 
 namespace krea {
@@ -125,6 +126,32 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int64_t attention_items(const attn_args& a, int q_tokens) {
   return (int64_t)((q_tokens + 63) / 64) * (a.heads_q / 4) * a.batch;
+}
+
+std::vector<int32_t> scan_item_order(const attn_args& a, const Plan& p, int q_begin, int q_end) {
+  const Layout& l = p.lay;
+  const int nq = (q_end - q_begin + 63) / 64;
+  const int64_t total = attention_items(a, q_end - q_begin);
+  std::vector<int32_t> cost(nq, 0);
+  for (int qt = 0; qt < nq; ++qt) {
+    const int lo = q_begin + 64 * qt, hi = std::min(lo + 64, q_end);
+    const bool any = lo < std::min(hi, l.text) || std::max(lo, l.t_pad) < std::min(hi, l.t_pad + l.image);
+    const int qa = lo / kTile;
+    cost[qt] = any ? p.row_ptr[qa + 1] - p.row_ptr[qa] : 0;
+  }
+  std::vector<int32_t> order((size_t)total);
+  const int64_t per = total / 8, rem = total % 8;
+  std::vector<int32_t> range;
+  for (int x = 0; x < 8; ++x) {
+    const int64_t base = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+    const int64_t cnt = x < rem ? per + 1 : per;
+    range.resize((size_t)cnt);
+    for (int64_t i = 0; i < cnt; ++i) range[(size_t)i] = (int32_t)(base + i);
+    std::stable_sort(range.begin(), range.end(),
+                     [&](int32_t u, int32_t v) { return cost[u % nq] > cost[v % nq]; });
+    for (int64_t i = 0; i < cnt; ++i) order[(size_t)(x + 8 * i)] = range[(size_t)i];
+  }
+  return order;
 }
 
 WorkspaceLayout workspace_layout(const attn_args& a) {
@@ -280,6 +307,12 @@ Plan build_plan(const attn_args& a) {
       }
       p.row_ptr[qa + 1] = (int32_t)p.cols.size();
     }
+    const int chunk = a.q_chunk > 0 ? a.q_chunk : p.lay.length;
+    for (int q0 = 0; q0 < p.lay.length; q0 += chunk) {
+      p.slice_begin.push_back((int32_t)p.item_order.size());
+      const std::vector<int32_t> o = scan_item_order(a, p, q0, std::min(p.lay.length, q0 + chunk));
+      p.item_order.insert(p.item_order.end(), o.begin(), o.end());
+    }
   } else {
     p.active_tiles = (int64_t)nb * nb;
     p.partial_tiles = (p.lay.n % kTile) ? nb : 0;
@@ -295,6 +328,9 @@ std::string plan_key(const attn_args& a) {
                 tm ? a.percentage : -1.0, tm ? a.band_blocks : -1,
                 (unsigned long long)(tm ? a.seed : 0), sc ? a.window : -1,
                 sc ? a.tile_aligned : -1);
+  if (sc)  // the scanline launch order depends on the item count of each slice
+    std::snprintf(buf + std::strlen(buf), sizeof(buf) - std::strlen(buf), " b%d hq%d qc%d", a.batch, a.heads_q,
+                  a.q_chunk);
   return std::string(buf);
 }
 

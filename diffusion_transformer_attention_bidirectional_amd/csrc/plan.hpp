@@ -40,6 +40,11 @@ struct Plan {
   std::vector<int32_t> row_ptr;
   std::vector<int32_t> cols;
   std::vector<int32_t> full_count;
+  // Scanline: the order in which each launch (query slice) runs its work items,
+  // item_order[slice_begin[s] + L] being the item of workgroup L of slice s (see
+  // scan_item_order).
+  std::vector<int32_t> item_order;
+  std::vector<int32_t> slice_begin;
   int64_t int8_tiles = 0, active_tiles = 0, partial_tiles = 0;
 };
 
@@ -56,6 +61,15 @@ constexpr size_t kTailPartBytes = (size_t)kTailWaves * kTailFloats * 64 * sizeof
 // Work items of one attention launch over `q_tokens` logical query positions:
 // 64-token query tiles x groups of 4 query heads x batch.
 int64_t attention_items(const attn_args& a, int q_tokens);
+
+// Workgroup -> work item order of a scanline launch over logical query rows
+// [q_begin, q_end).  Item t is (query tile t % nq, head group (t / nq) % G4, batch); the
+// hardware hands workgroup L to XCD L % 8, and workgroup L = x + 8 i runs the i-th item
+// of XCD x's contiguous range of items (so the items of one KV head share an L2, as in
+// the dense order).  Within each range the items run longest first (by key tiles, stable
+// for equal lengths): query tiles of text rows visit every key tile, image rows only
+// their band, and an order that starts the long items late leaves a tail.
+std::vector<int32_t> scan_item_order(const attn_args& a, const Plan& p, int q_begin, int q_end);
 
 // Offsets of the workspace regions (bytes, 256-aligned).  Every mode holds V^T tiles
 // [B, Hkv, nb, 128 channels, 128 keys] and the key-norm bounds; dense and TileMix add the tail-split counters

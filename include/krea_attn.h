@@ -133,6 +133,14 @@ attn_status attn_plan_info_get(const attn_args* args, attn_plan_info* out);
 attn_status attn_route_map(const attn_args* args, uint8_t* out, int32_t nb);
 /* Scanline block mask, row-major uint8 [nb][nb] over logical tiles: 0 skip, 1 full, 2 partial. */
 attn_status attn_block_mask(const attn_args* args, uint8_t* out, int32_t nb);
+/* Scanline launch order of query slice `slice` (slices of q_chunk logical rows, one
+ * launch each): out[L] = the work item that workgroup L runs, for the n workgroups of the
+ * launch (n = ceil(slice rows / 64) * heads_q / 4 * batch; item t = query tile t % nq,
+ * head group (t / nq) % (heads_q / 4), batch t / (nq * heads_q / 4)).  Workgroup L goes
+ * to XCD L % 8, which runs a contiguous range of items, longest first (the number of key
+ * tiles the Scanline mask gives the tile's query block: "What the mask actually is").
+ * Errors: not ATTN_SCANLINE, slice out of range, n not the launch's size, out NULL. */
+attn_status attn_item_order(const attn_args* args, int32_t slice, int32_t* out, int64_t n);
 
 /* Device debug exports.  They run the same device functions as attn_forward.
  *

@@ -116,6 +116,53 @@ def test_block_mask_4mp_vs_oracle(lib):
     assert info["active_tiles"] == 2418 and info["partial_tiles"] == 0
 
 
+ORDER_CASES = [
+    # text, rows, cols, window, aligned, q_chunk, batch, heads_q
+    (512, 64, 64, 11, 1, 0, 1, 48),     # the 1 MP Scanline call
+    (512, 128, 128, 11, 1, 4096, 1, 48),  # 4 MP, five query slices
+    (77, 9, 13, 3, 0, 256, 2, 8),        # ragged text, padding tiles, batch 2
+    (64, 8, 8, 1, 1, 0, 1, 4),           # fewer items than XCDs * CUs
+]
+
+
+@pytest.mark.parametrize("t,rows,cols,window,aligned,chunk,batch,hq", ORDER_CASES)
+def test_scanline_item_order(lib, t, rows, cols, window, aligned, chunk, batch, hq):
+    """Each launch runs a permutation of its items; XCD x (workgroups L = x + 8 i) runs its
+    contiguous range of items, longest first by the key tiles of the item's query block
+    (zero for a tile of padding only), ties in item order."""
+    args = ka.make_args(batch=batch, heads_q=hq, heads_kv=hq // 4, text_tokens=t, img_rows=rows, img_cols=cols,
+                        mode="scanline", window=window, tile_aligned=aligned, q_chunk=chunk)
+    mask = plan_ref.block_mask(t, rows, cols, window, bool(aligned))
+    lay = plan_ref.ScanLayout(t, rows, cols)
+    length = lay.length
+    step = chunk if chunk > 0 else length
+    for si, q0 in enumerate(range(0, length, step)):
+        q1 = min(length, q0 + step)
+        nq = (q1 - q0 + 63) // 64
+        n = nq * (hq // 4) * batch
+        order = ka.item_order(args, si)
+        assert order.shape == (n,) and sorted(order.tolist()) == list(range(n))
+
+        def cost(item):
+            lo = q0 + 64 * (item % nq)
+            hi = min(lo + 64, q1)
+            valid = lo < min(hi, t) or max(lo, lay.t_pad) < min(hi, lay.t_pad + rows * cols)
+            return int((mask[lo // 128] != 0).sum()) if valid else 0
+
+        per, rem = divmod(n, 8)
+        for x in range(8):
+            base = x * (per + 1) if x < rem else rem * (per + 1) + (x - rem) * per
+            cnt = per + 1 if x < rem else per
+            got = order[x::8].tolist()
+            assert len(got) == cnt and sorted(got) == list(range(base, base + cnt))
+            keys = [(-cost(i), i) for i in got]
+            assert keys == sorted(keys)
+    with pytest.raises(ka.KreaAttnError):
+        ka.item_order(args, len(range(0, length, step)))
+    dense = ka.make_args(text_tokens=t, img_rows=rows, img_cols=cols, mode="dense")
+    assert lib.attn_item_order(ctypes.byref(dense), 0, np.zeros(8, np.int32).ctypes.data, 8) == -1
+
+
 TAIL_PART_BYTES = 8 * 66 * 64 * 4  # 8 waves x (64 O values, max, sum) x 64 lanes, fp32
 
 
