@@ -871,52 +871,73 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
 //     scale = fp32(a / 127)); the attention kernel derives the same scales itself.
 template <bool BF16, int MODE, bool QUANT, bool QSCALE>
 __global__ void __launch_bounds__(256) prepass_kernel(const AttnParams p, uint16_t* v_t, const QuantParams qp) {
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * SLAB];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * SLAB];              // V tile, slab layout
+  __shared__ __attribute__((aligned(1024))) unsigned char klds[QUANT ? KT * 256 : 16];  // K tile, row-major
   __shared__ float kmax[4];
   const int kb = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int lane = tid & 63, lq = lane & 31, lh = lane >> 5, wave = tid >> 6;
   const int64_t bg = (int64_t)b * p.heads_kv + g;
+  // Every load of the block goes out first, so the pass waits for memory once: thread
+  // tid takes the 16-byte chunk c = id % 16 of row id / 16 of both tiles, id = tid + 256 i
+  // (the 16 chunks of a row are 16 consecutive lanes of one wave).
+  const bool need_k = p.k_norm != nullptr || (QUANT && qp.smooth_k);
+  uint4 kx[8], vx[8];
+  const uint16_t* kbase = (const uint16_t*)p.k.ptr + (int64_t)b * p.k.sb + (int64_t)g * p.k.sh;
+  const uint16_t* vbase = (const uint16_t*)p.v.ptr + (int64_t)b * p.v.sb + (int64_t)g * p.v.sh;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int id = tid + 256 * i;
+    const int row = id >> 4, c = id & 15;
+    const int t = kb * KT + row;
+    const bool valid = tok_valid<MODE>(p, t);
+    const int64_t ph = valid ? tok_phys<MODE>(p, t) : 0;
+    kx[i] = need_k && valid ? *(const uint4*)(kbase + ph * p.k.st + c * 8) : make_uint4(0, 0, 0, 0);
+    vx[i] = v_t != nullptr && valid ? *(const uint4*)(vbase + ph * p.v.st + c * 8) : make_uint4(0, 0, 0, 0);
+  }
   // the attention launches that follow start from zero tail counters
   if (p.tail_count != nullptr && kb == 0 && g == 0 && b == 0) p.tail_count[tid] = 0;  // 256 counters
-  if (p.k_norm != nullptr) {
-    // largest |k| over the block's keys (two threads per key, 64 channels each), rounded up
-    const int t = kb * KT + (tid >> 1);
-    float ss = 0.f;
-    if (tok_valid<MODE>(p, t)) {
-      const uint16_t* kr = (const uint16_t*)p.k.ptr + (int64_t)b * p.k.sb + (int64_t)g * p.k.sh +
-                           (int64_t)tok_phys<MODE>(p, t) * p.k.st + (tid & 1) * 64;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const uint4 x = *(const uint4*)(kr + 8 * c);
-        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x0 = elem_to_f32<BF16>(w[e] & 0xffff), x1 = elem_to_f32<BF16>(w[e] >> 16);
-          ss = fmaf(x0, x0, ss);
-          ss = fmaf(x1, x1, ss);
-        }
-      }
-    }
-    ss += __shfl_xor(ss, 1);
-#pragma unroll
-    for (int o = 32; o >= 2; o >>= 1) ss = fmaxf(ss, __shfl_xor(ss, o));
-    if (lane == 0) kmax[wave] = ss;
-    __syncthreads();
-    if (tid == 0)
-      p.k_norm[bg * p.nb + kb] = __builtin_sqrtf(fmaxf(fmaxf(kmax[0], kmax[1]), fmaxf(kmax[2], kmax[3]))) * 1.001f;
-  }
   if (v_t != nullptr) {
-    const uint16_t* vbase = (const uint16_t*)p.v.ptr + (int64_t)b * p.v.sb + (int64_t)g * p.v.sh;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int id = tid + 256 * i;
       const int row = id >> 4, c = id & 15;
-      const int t = kb * KT + row;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (tok_valid<MODE>(p, t)) x = *(const uint4*)(vbase + (int64_t)tok_phys<MODE>(p, t) * p.v.st + c * 8);
-      *(uint4*)(lds + (c >> 2) * SLAB + row * 64 + (c & 3) * 16) = x;
+      *(uint4*)(lds + (c >> 2) * SLAB + row * 64 + (c & 3) * 16) = vx[i];
     }
-    __syncthreads();
+  }
+  if (QUANT && qp.smooth_k) {
+    // rows past n are zero, so they add nothing to the column sums
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int id = tid + 256 * i;
+      *(uint4*)(klds + (id >> 4) * 256 + (id & 15) * 16) = kx[i];
+    }
+  }
+  if (p.k_norm != nullptr) {
+    // largest |k| over the block's keys, rounded up: each row's squared norm is summed over
+    // its 16 lanes, then the maximum taken over rows
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t w[4] = {kx[i].x, kx[i].y, kx[i].z, kx[i].w};
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = elem_to_f32<BF16>(w[e] & 0xffff), x1 = elem_to_f32<BF16>(w[e] >> 16);
+        ss = fmaf(x0, x0, ss);
+        ss = fmaf(x1, x1, ss);
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o);
+      mx = fmaxf(mx, ss);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (lane == 0) kmax[wave] = mx;
+  }
+  __syncthreads();
+  if (p.k_norm != nullptr && tid == 0)
+    p.k_norm[bg * p.nb + kb] = __builtin_sqrtf(fmaxf(fmaxf(kmax[0], kmax[1]), fmaxf(kmax[2], kmax[3]))) * 1.001f;
+  if (v_t != nullptr) {
     const int db = tid >> 6;
     uint16_t* dst = v_t + ((bg * p.nb + kb) * 128 + 32 * db + lq) * 128;
 #pragma unroll
@@ -927,30 +948,14 @@ __global__ void __launch_bounds__(256) prepass_kernel(const AttnParams p, uint16
   }
   if (QUANT) {
     // TileMix layouts are unpadded: token t of the block is row t of the tensors, valid
-    // when t < n
-    if (qp.smooth_k) {
-      // K tile rows into LDS ([128 tokens][256 B], zero rows past n), then one thread per
-      // channel adds the block's tokens in order
-      __syncthreads();  // the V^T transpose reads of the LDS are done
-      const uint16_t* kbase = (const uint16_t*)qp.k.ptr + (int64_t)b * qp.k.sb + (int64_t)g * qp.k.sh;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int id = tid + 256 * i;
-        const int row = id >> 4, c = id & 15;
-        const int t = kb * KT + row;
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if (t < qp.n) x = *(const uint4*)(kbase + (int64_t)t * qp.k.st + c * 8);
-        *(uint4*)(lds + row * 256 + c * 16) = x;
-      }
-      __syncthreads();
-      if (tid < 128) {
-        const int rows = min(KT, qp.n - kb * KT);
-        double acc = 0.0;
+    // when t < n.  smooth_k: one thread per channel adds the block's tokens in order.
+    if (qp.smooth_k && tid < 128) {
+      const int rows = min(KT, qp.n - kb * KT);
+      double acc = 0.0;
 #pragma unroll 16
-        for (int r = 0; r < rows; ++r)
-          acc = __dadd_rn(acc, (double)elem_to_f32<BF16>(*(const uint16_t*)(lds + r * 256 + tid * 2)));
-        qp.k_part[(bg * qp.nb + kb) * 128 + tid] = acc;
-      }
+      for (int r = 0; r < rows; ++r)
+        acc = __dadd_rn(acc, (double)elem_to_f32<BF16>(*(const uint16_t*)(klds + r * 256 + tid * 2)));
+      qp.k_part[(bg * qp.nb + kb) * 128 + tid] = acc;
     }
     // Q tile scales (the attention kernel computes its own): wave w takes the query heads
     // w, w + 4, ... of this KV head
