@@ -28,7 +28,7 @@ PATTERNS = {"zero": 0, "one": 1, "band": 2, "all": 3}
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported dtype", -3: "unsupported shape",
           -4: "workspace too small", -5: "device error"}
 
-EXPORTS = ("attn_workspace_bytes", "attn_forward", "attn_plan_info_get", "attn_route_map",
+EXPORTS = ("attn_workspace_bytes", "attn_forward", "attn_forward_gated", "attn_plan_info_get", "attn_route_map",
            "attn_block_mask", "attn_item_order", "attn_quantize", "attn_int8_scores", "attn_mask_row_counts",
            "attn_set_kernel_events", "attn_status_string", "attn_last_error")
 
@@ -82,6 +82,8 @@ def load_library(path: str = LIB_PATH):
     sig = {
         "attn_workspace_bytes": [P(AttnArgs), P(sz)],
         "attn_forward": [P(AttnArgs), P(AttnTensor), P(AttnTensor), P(AttnTensor), P(AttnTensor), vp, sz, vp],
+        "attn_forward_gated": [P(AttnArgs), P(AttnTensor), P(AttnTensor), P(AttnTensor), P(AttnTensor),
+                               P(AttnTensor), vp, sz, vp],
         "attn_plan_info_get": [P(AttnArgs), P(AttnPlanInfo)],
         "attn_route_map": [P(AttnArgs), vp, i32],
         "attn_block_mask": [P(AttnArgs), vp, i32],
@@ -158,10 +160,11 @@ def args_for(q, k, *, text_tokens, img_rows=0, img_cols=0, **kw) -> AttnArgs:
 
 
 def attention(q, k, v, *, text_tokens, img_rows=0, img_cols=0, mode="dense", out=None, workspace=None,
-              stream=None, **kw):
+              stream=None, gate=None, **kw):
     """O = attention(q, k, v) on the GPU.  q [B, N, Hq, 128], k/v [B, N, Hkv, 128], bf16 or fp16,
-    N = text_tokens + img_rows * img_cols.  Extra keywords as in make_args().  Asynchronous on
-    the current (or given) stream."""
+    N = text_tokens + img_rows * img_cols.  With ``gate`` (shaped like q), O * sigmoid(gate)
+    (attn_forward_gated).  Extra keywords as in make_args().  Asynchronous on the current (or
+    given) stream."""
     import torch
     args = args_for(q, k, text_tokens=text_tokens, img_rows=img_rows, img_cols=img_cols, mode=mode, **kw)
     if out is None:
@@ -171,9 +174,16 @@ def attention(q, k, v, *, text_tokens, img_rows=0, img_cols=0, mode="dense", out
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     wptr = workspace.data_ptr() if workspace is not None else None
     wlen = workspace.numel() if workspace is not None else 0
-    _check(load_library().attn_forward(ctypes.byref(args), ctypes.byref(_tensor(q)), ctypes.byref(_tensor(k)),
-                                       ctypes.byref(_tensor(v)), ctypes.byref(_tensor(out)), wptr, wlen,
-                                       _stream_handle(stream, q.device)))
+    lib = load_library()
+    tq, tk, tv, to = (ctypes.byref(_tensor(t)) for t in (q, k, v, out))
+    st = _stream_handle(stream, q.device)
+    if gate is None:
+        _check(lib.attn_forward(ctypes.byref(args), tq, tk, tv, to, wptr, wlen, st))
+    else:
+        if tuple(gate.shape) != tuple(q.shape) or gate.dtype != q.dtype:
+            raise KreaAttnError("gate must have q's shape and dtype")
+        _check(lib.attn_forward_gated(ctypes.byref(args), tq, tk, tv, ctypes.byref(_tensor(gate)), to, wptr, wlen,
+                                      st))
     return out
 
 

@@ -252,12 +252,17 @@ attn_status attn_workspace_bytes(const attn_args* args, size_t* bytes) {
   return ATTN_OK;
 }
 
-attn_status attn_forward(const attn_args* args, const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
-                         const attn_tensor* o, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+attn_status forward_impl(const attn_args* args, const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                         const attn_tensor* gate, const attn_tensor* o, void* workspace, size_t workspace_bytes,
+                         void* stream) {
   attn_status s = check_args(args);
   if (s != ATTN_OK) return s;
   if ((s = check_tensor(q, "q")) || (s = check_tensor(k, "k")) || (s = check_tensor(v, "v")) ||
-      (s = check_tensor(o, "o")))
+      (s = check_tensor(o, "o")) || (gate && (s = check_tensor(gate, "gate"))))
     return s;
   const attn_args& a = *args;
   if (k->stride_t >= (1 << 23))
@@ -277,6 +282,12 @@ attn_status attn_forward(const attn_args* args, const attn_tensor* q, const attn
   p.o_sb = o->stride_b;
   p.o_st = o->stride_t;
   p.o_sh = o->stride_h;
+  if (gate) {
+    p.gate = gate->ptr;
+    p.g_sb = gate->stride_b;
+    p.g_st = gate->stride_t;
+    p.g_sh = gate->stride_h;
+  }
   const bool bf16 = a.dtype == ATTN_BF16;
   p.v_t = (const uint16_t*)((unsigned char*)workspace + w.v_t);
   p.k_norm = (float*)((unsigned char*)workspace + w.k_norm);
@@ -318,6 +329,23 @@ attn_status attn_forward(const attn_args* args, const attn_tensor* q, const attn
   g_err.clear();
   return ATTN_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_forward(const attn_args* args, const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                         const attn_tensor* o, void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_impl(args, q, k, v, nullptr, o, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_forward_gated(const attn_args* args, const attn_tensor* q, const attn_tensor* k,
+                               const attn_tensor* v, const attn_tensor* gate, const attn_tensor* o,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (!gate) return fail(ATTN_ERR_INVALID_ARG, "gate is NULL");
+  return forward_impl(args, q, k, v, gate, o, workspace, workspace_bytes, stream);
+}
+
 
 attn_status attn_plan_info_get(const attn_args* args, attn_plan_info* out) {
   attn_status s = check_args(args);

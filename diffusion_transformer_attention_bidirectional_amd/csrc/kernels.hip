@@ -838,19 +838,35 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
     if (tid == 0) p.tail_count[wi.slot] = 0;  // ready for the next launch
   }
 
-  // ---- epilogue: O = O^T / l, rows of valid queries only (padding is never written)
+  // ---- epilogue: O = O^T / l, rows of valid queries only (padding is never written); with
+  // a gate, O * sigmoid(gate) ("LayerStream: Krea2 Chunking", "What the node does to the
+  // block": the attention gate is applied before the output projection), in fp32 before
+  // the one rounding to the output dtype
   const float lt = ws.l + __shfl_xor(ws.l, 32);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   if (qinfo.valid) {
-    uint16_t* dst = (uint16_t*)p.o + (int64_t)b * p.o_sb + (int64_t)tok_phys<MODE>(p, tq) * p.o_st +
-                    (int64_t)h * p.o_sh;
+    const int64_t tp = tok_phys<MODE>(p, tq);
+    uint16_t* dst = (uint16_t*)p.o + (int64_t)b * p.o_sb + tp * p.o_st + (int64_t)h * p.o_sh;
+    const uint16_t* gsrc = p.gate == nullptr ? nullptr
+                                             : (const uint16_t*)p.gate + (int64_t)b * p.g_sb + tp * p.g_st +
+                                                   (int64_t)h * p.g_sh;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
         const f32x16& o = ws.O[db];
-        const uint2 val = make_uint2(pack2<BF16>(o[4 * grp] * inv, o[4 * grp + 1] * inv),
-                                     pack2<BF16>(o[4 * grp + 2] * inv, o[4 * grp + 3] * inv));
+        float f[4] = {o[4 * grp] * inv, o[4 * grp + 1] * inv, o[4 * grp + 2] * inv, o[4 * grp + 3] * inv};
+        if (gsrc != nullptr) {
+          const uint2 gv = *(const uint2*)(gsrc + 32 * db + 8 * grp + 4 * lh);
+          const uint32_t gw[2] = {gv.x, gv.y};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float gx = elem_to_f32<BF16>((uint16_t)(gw[e >> 1] >> (16 * (e & 1))));
+            // sigmoid(g) = 1 / (1 + 2^(-g log2 e)); 2^(+large) = inf gives 0, 2^(-large) = 0 gives 1
+            f[e] *= __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gx * 1.4426950408889634f));
+          }
+        }
+        const uint2 val = make_uint2(pack2<BF16>(f[0], f[1]), pack2<BF16>(f[2], f[3]));
         *(uint2*)(dst + 32 * db + 8 * grp + 4 * lh) = val;
       }
   }

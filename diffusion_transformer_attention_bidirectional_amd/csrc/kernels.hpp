@@ -17,6 +17,9 @@ struct AttnParams {
   TensorRef q, k, v;
   void* o;
   int64_t o_sb, o_st, o_sh;
+  // optional attention gate [B, N, Hq, d] (input dtype): o = attention * sigmoid(gate)
+  const void* gate;
+  int64_t g_sb, g_st, g_sh;
   int batch, heads_q, heads_kv, group;  // group = heads_q / heads_kv
   int n;        // physical tokens
   int text;     // T

@@ -127,6 +127,17 @@ attn_status attn_forward(const attn_args* args, const attn_tensor* q, const attn
                          const attn_tensor* v, const attn_tensor* o, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* The attention call with the block's attention gate applied as the output is stored
+ * ("LayerStream: Krea2 Chunking", "What the node does to the block": pass two computes the
+ * attention gate beside q and applies it before the output projection):
+ * o = attention(q, k, v) * sigmoid(gate), elementwise, in fp32 before the one rounding to
+ * the input dtype.  gate: [B, N, Hq, 128] in the input dtype, with its own element strides
+ * (head_dim contiguous, 16-byte aligned), read only.  Everything else as attn_forward.
+ * Errors: those of attn_forward; gate NULL or misaligned is ATTN_ERR_INVALID_ARG. */
+attn_status attn_forward_gated(const attn_args* args, const attn_tensor* q, const attn_tensor* k,
+                               const attn_tensor* v, const attn_tensor* gate, const attn_tensor* o,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Host-only plan exports (no GPU needed). */
 attn_status attn_plan_info_get(const attn_args* args, attn_plan_info* out);
 /* TileMix route map, row-major uint8 [nb][nb] over (query block, key block): 0 FP16, 1 INT8. */

@@ -142,3 +142,34 @@ def text_outlier_case(w: Workload, text_scale: float = 4.0, outlier_channel: int
     kf[:, :t, :, outlier_channel] = outlier_value
     dt = _TORCH_DTYPE[w.dtype]
     return qf.to(dt), kf.to(dt), v
+
+
+def make_gate(shape, dtype: str, seed: int, std: float = 2.0) -> torch.Tensor:
+    """A seeded attention-gate tensor of the given shape (N(0, std) drawn in float32, cast by
+    round-to-nearest-even), as a CPU tensor in ``dtype``."""
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal(tuple(shape), dtype=np.float32) * np.float32(std)
+    return torch.from_numpy(g).to(_TORCH_DTYPE[dtype])
+
+
+def make_block_inputs(w: Workload, d_model: int, seed: int):
+    """Seeded inputs of one block's attention context for workload ``w`` (heads and tokens
+    from ``w``): x [B, N, D] ~ N(0, 1); W_q, W_gate [D, Hq d], W_k, W_v [D, Hkv d] and W_o
+    [Hq d, D] ~ N(0, 1/D) and N(0, 1/(Hq d)) (unit-variance projections of unit-variance
+    rows); y0 [B, N, D] ~ N(0, 1), the residual the context is added into.  CPU tensors in
+    w.dtype, drawn in this order."""
+    rng = np.random.default_rng(seed)
+    n, hq, hkv, d = w.tokens, w.heads_q, w.heads_kv, w.head_dim
+    dt = _TORCH_DTYPE[w.dtype]
+
+    def draw(shape, std):
+        return torch.from_numpy(rng.standard_normal(shape, dtype=np.float32) * np.float32(std)).to(dt)
+
+    x = draw((w.batch, n, d_model), 1.0)
+    wq = draw((d_model, hq * d), d_model ** -0.5)
+    wk = draw((d_model, hkv * d), d_model ** -0.5)
+    wv = draw((d_model, hkv * d), d_model ** -0.5)
+    wg = draw((d_model, hq * d), d_model ** -0.5)
+    wo = draw((hq * d, d_model), (hq * d) ** -0.5)
+    y0 = draw((w.batch, n, d_model), 1.0)
+    return x, wq, wk, wv, wg, wo, y0

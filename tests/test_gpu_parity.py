@@ -9,8 +9,8 @@ import pytest
 import torch
 
 import diffusion_transformer_attention_bidirectional_amd as ka
-from oracle import attn_ref, plan_ref, quant_ref
-from synth import WORKLOADS, Workload, make_qkv, text_outlier_case, to_f64
+from oracle import attn_ref, block_ref, plan_ref, quant_ref
+from synth import WORKLOADS, Workload, make_gate, make_qkv, text_outlier_case, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -113,6 +113,35 @@ def test_slices_match_unsliced(dev, w):
             # a slice's last wave of work items may split its key ranges differently from
             # the unsliced launch, which moves only the final rounding to bf16
             assert np.all(np.abs(sliced - full) <= 2.0 ** -7 * np.abs(full) + 1e-6)
+
+
+GATED = [
+    ("dense", _w()),
+    ("tilemix", _w(mode="tilemix", pattern="band", percentage=0.6, band_blocks=1, smooth_k=True, text_tokens=130,
+                   img_rows=12, img_cols=40)),
+    ("scanline", _w(mode="scanline", window=3, tile_aligned=False, text_tokens=77)),
+    ("dense_f16_sliced", _w(dtype="f16", q_chunk=128)),
+]
+
+
+@pytest.mark.parametrize("name,w", GATED, ids=[n for n, _ in GATED])
+def test_gated_vs_oracle(dev, name, w):
+    """attn_forward_gated: attention * sigmoid(gate), the gate of the block's pass two."""
+    q, k, v = make_qkv(w)
+    gate = make_gate(q.shape, w.dtype, seed=99)
+    got, _ = _run(w, dev, q, k, v, gate=gate.to(dev))
+    ref = attn_ref.attention(to_f64(q), to_f64(k), to_f64(v), w) * block_ref.sigmoid(to_f64(gate))
+    mx, mn, rel = _assert_close(got, ref, name)
+    print(f"gated {name}: max {mx:.2e} mean {mn:.2e} rel {rel:.2e}")
+
+
+def test_gate_zero_halves_exactly(dev):
+    """sigmoid(0) is 1/2 in the kernel too, and halving commutes with the rounding."""
+    w = _w()
+    plain, qkv = _run(w, dev)
+    gate = torch.zeros(qkv[0].shape, dtype=qkv[0].dtype)
+    gated, _ = _run(w, dev, *qkv, gate=gate.to(dev))
+    assert (gated == 0.5 * plain).all()
 
 
 def test_zero_pattern_bit_identical_to_dense(dev):
