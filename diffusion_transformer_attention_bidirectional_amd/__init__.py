@@ -28,7 +28,8 @@ PATTERNS = {"zero": 0, "one": 1, "band": 2, "all": 3}
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported dtype", -3: "unsupported shape",
           -4: "workspace too small", -5: "device error"}
 
-EXPORTS = ("attn_workspace_bytes", "attn_forward", "attn_forward_gated", "attn_plan_info_get", "attn_route_map",
+EXPORTS = ("attn_workspace_bytes", "attn_forward", "attn_forward_gated", "attn_block_workspace_bytes",
+           "attn_block_forward", "attn_plan_info_get", "attn_route_map",
            "attn_block_mask", "attn_item_order", "attn_quantize", "attn_int8_scores", "attn_mask_row_counts",
            "attn_set_kernel_events", "attn_status_string", "attn_last_error")
 
@@ -58,6 +59,13 @@ class AttnTensor(ctypes.Structure):
                 ("stride_h", ctypes.c_int64)]
 
 
+class AttnBlockWeights(ctypes.Structure):
+    """attn_block_weights: device pointers of W_q, W_k, W_v, W_gate [D, out] and W_o [Hq d, D]."""
+    _fields_ = [("w_q", ctypes.c_void_p), ("w_k", ctypes.c_void_p), ("w_v", ctypes.c_void_p),
+                ("w_gate", ctypes.c_void_p), ("w_o", ctypes.c_void_p), ("model_dim", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
 class AttnPlanInfo(ctypes.Structure):
     _fields_ = [("n_blocks", ctypes.c_int32), ("text_blocks", ctypes.c_int32),
                 ("logical_tokens", ctypes.c_int32), ("text_pad", ctypes.c_int32),
@@ -84,6 +92,8 @@ def load_library(path: str = LIB_PATH):
         "attn_forward": [P(AttnArgs), P(AttnTensor), P(AttnTensor), P(AttnTensor), P(AttnTensor), vp, sz, vp],
         "attn_forward_gated": [P(AttnArgs), P(AttnTensor), P(AttnTensor), P(AttnTensor), P(AttnTensor),
                                P(AttnTensor), vp, sz, vp],
+        "attn_block_workspace_bytes": [P(AttnArgs), i32, P(sz)],
+        "attn_block_forward": [P(AttnArgs), P(AttnBlockWeights), vp, vp, vp, sz, vp],
         "attn_plan_info_get": [P(AttnArgs), P(AttnPlanInfo)],
         "attn_route_map": [P(AttnArgs), vp, i32],
         "attn_block_mask": [P(AttnArgs), vp, i32],
@@ -185,6 +195,35 @@ def attention(q, k, v, *, text_tokens, img_rows=0, img_cols=0, mode="dense", out
         _check(lib.attn_forward_gated(ctypes.byref(args), tq, tk, tv, ctypes.byref(_tensor(gate)), to, wptr, wlen,
                                       st))
     return out
+
+
+def block_workspace_bytes(args: AttnArgs, model_dim: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().attn_block_workspace_bytes(ctypes.byref(args), int(model_dim), ctypes.byref(n)))
+    return n.value
+
+
+def block_forward(x, wq, wk, wv, wg, wo, y, *, text_tokens, img_rows=0, img_cols=0, heads_q, heads_kv, mode="dense",
+                  workspace=None, stream=None, **kw):
+    """y += (attention(x W_q, x W_k, x W_v) * sigmoid(x W_gate)) W_o on the GPU, in the two passes of
+    attn_block_forward.  x, y: [B, N, D] contiguous; W_q, W_gate [D, Hq 128], W_k, W_v [D, Hkv 128],
+    W_o [Hq 128, D]; all in one dtype (bf16 or fp16) on one device.  Returns y."""
+    import torch
+    tensors = (x, wq, wk, wv, wg, wo, y)
+    if any(not t.is_contiguous() or t.dtype != x.dtype or t.device != x.device for t in tensors):
+        raise KreaAttnError("x, y and the weights must be contiguous, of one dtype and on one device")
+    b, n, d_model = x.shape
+    args = make_args(batch=b, heads_q=heads_q, heads_kv=heads_kv, text_tokens=text_tokens, img_rows=img_rows,
+                     img_cols=img_cols, dtype=_dtype_name(x), mode=mode, **kw)
+    weights = AttnBlockWeights(wq.data_ptr(), wk.data_ptr(), wv.data_ptr(), wg.data_ptr(), wo.data_ptr(),
+                               int(d_model), 0)
+    nbytes = block_workspace_bytes(args, d_model)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    _check(load_library().attn_block_forward(ctypes.byref(args), ctypes.byref(weights), ctypes.c_void_p(x.data_ptr()),
+                                             ctypes.c_void_p(y.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
+                                             workspace.numel(), _stream_handle(stream, x.device)))
+    return y
 
 
 def set_kernel_events(start=None, stop=None):

@@ -1,7 +1,8 @@
 """Build libkrea_attn.so for gfx950 (MI355X) in this package directory.
 
-Three translation units: the host planner (plan.cpp) and the C ABI (capi.cpp) as host
-C++, the kernels (kernels.hip) as HIP for gfx950.  Flags:
+Four translation units: the host planner (plan.cpp), the C ABI (capi.cpp) and the block
+path's GEMM calls (gemm.cpp, linked against hipBLASLt) as host C++, the kernels
+(kernels.hip) as HIP for gfx950.  Flags:
   -Xclang -target-feature -Xclang -packed-fp32-ops  no packed fp32 VALU instructions
   -mllvm -amdgpu-mfma-vgpr-form                      keep MFMA results in VGPRs (the
       softmax reads the score accumulators directly; AGPR results would need a
@@ -50,16 +51,18 @@ def build(verbose: bool = False) -> str:
     units = [
         ("plan.cpp", COMMON),
         ("capi.cpp", COMMON + ["-D__HIP_PLATFORM_AMD__"]),
+        ("gemm.cpp", COMMON + ["-D__HIP_PLATFORM_AMD__"]),
         ("kernels.hip", COMMON + DEVICE),
     ]
     jobs = []
     for src, flags in units:
         obj = os.path.join(BUILD, src + ".o")
         jobs.append(([cc] + flags + ["-c", os.path.join(CSRC, src), "-o", obj], obj))
-    with concurrent.futures.ThreadPoolExecutor(max_workers=3) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
         list(ex.map(lambda j: _run(j[0]), jobs))
     tmp = LIB + ".tmp"
-    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [o for _, o in jobs])
+    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [o for _, o in jobs] +
+         ["-L/opt/rocm/lib", "-lhipblaslt"])
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

@@ -12,6 +12,7 @@
 #include <mutex>
 #include <string>
 
+#include "gemm.hpp"
 #include "kernels.hpp"
 #include "krea_attn.h"
 #include "plan.hpp"
@@ -256,9 +257,24 @@ attn_status attn_workspace_bytes(const attn_args* args, size_t* bytes) {
 
 namespace {
 
-attn_status forward_impl(const attn_args* args, const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
-                         const attn_tensor* gate, const attn_tensor* o, void* workspace, size_t workspace_bytes,
-                         void* stream) {
+// One attention call after validation and its pre-work (pre-pass, quantiser), ready to
+// launch its query slices: the block path changes q, gate and o between slices.
+struct Prepared {
+  krea::AttnParams p;
+  std::shared_ptr<DevicePlan> dp;
+  krea::WorkspaceLayout w;
+  attn_args a;
+  hipStream_t st = nullptr;
+  bool bf16 = true;
+  int cus = 0, length = 0, chunk = 0;
+  int slices() const { return (length + chunk - 1) / chunk; }
+};
+
+void set_output(krea::AttnParams& p, const attn_tensor* o, const attn_tensor* gate);
+
+attn_status prepare(const attn_args* args, const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                    const attn_tensor* gate, const attn_tensor* o, void* workspace, size_t workspace_bytes,
+                    void* stream, Prepared* out) {
   attn_status s = check_args(args);
   if (s != ATTN_OK) return s;
   if ((s = check_tensor(q, "q")) || (s = check_tensor(k, "k")) || (s = check_tensor(v, "v")) ||
@@ -278,16 +294,7 @@ attn_status forward_impl(const attn_args* args, const attn_tensor* q, const attn
   p.q = ref(q);
   p.k = ref(k);
   p.v = ref(v);
-  p.o = o->ptr;
-  p.o_sb = o->stride_b;
-  p.o_st = o->stride_t;
-  p.o_sh = o->stride_h;
-  if (gate) {
-    p.gate = gate->ptr;
-    p.g_sb = gate->stride_b;
-    p.g_st = gate->stride_t;
-    p.g_sh = gate->stride_h;
-  }
+  set_output(p, o, gate);
   const bool bf16 = a.dtype == ATTN_BF16;
   p.v_t = (const uint16_t*)((unsigned char*)workspace + w.v_t);
   p.k_norm = (float*)((unsigned char*)workspace + w.k_norm);
@@ -312,22 +319,91 @@ attn_status forward_impl(const attn_args* args, const attn_tensor* q, const attn
       return s;
     if (a.mode == ATTN_TILEMIX) p.route = nullptr;  // all FP16: the TileMix kernel never looks at INT8 state
   }
-  const int length = dp->plan.lay.length;
-  const int chunk = a.q_chunk > 0 ? a.q_chunk : length;
-  const int mode = a.mode;
-  if (g_ev_start && (s = hip_check(hipEventRecord(g_ev_start, st), "timing event")) != ATTN_OK) return s;
-  const int cus = a.mode != ATTN_SCANLINE ? cu_count() : 0;
-  for (int q0 = 0, slice = 0; q0 < length; q0 += chunk, ++slice) {
-    p.q_begin = q0;
-    p.q_end = std::min(length, q0 + chunk);
-    plan_tail(p, krea::attention_items(a, p.q_end - p.q_begin), dp->plan.lay.nb, cus, w.tail_parts);
-    if (!dp->plan.item_order.empty())
-      p.item_order = (const int32_t*)(dp->dmem + dp->order_off) + dp->plan.slice_begin[slice];
-    if ((s = hip_check(krea::launch_attention(p, mode, bf16, st), "attention launch")) != ATTN_OK) return s;
-  }
-  if (g_ev_stop && (s = hip_check(hipEventRecord(g_ev_stop, st), "timing event")) != ATTN_OK) return s;
+  out->p = p;
+  out->dp = dp;
+  out->w = w;
+  out->a = a;
+  out->st = st;
+  out->bf16 = bf16;
+  out->cus = a.mode != ATTN_SCANLINE ? cu_count() : 0;
+  out->length = dp->plan.lay.length;
+  out->chunk = a.q_chunk > 0 ? a.q_chunk : out->length;
+  return ATTN_OK;
+}
+
+void set_output(krea::AttnParams& p, const attn_tensor* o, const attn_tensor* gate) {
+  p.o = o->ptr;
+  p.o_sb = o->stride_b;
+  p.o_st = o->stride_t;
+  p.o_sh = o->stride_h;
+  p.gate = gate ? gate->ptr : nullptr;
+  p.g_sb = gate ? gate->stride_b : 0;
+  p.g_st = gate ? gate->stride_t : 0;
+  p.g_sh = gate ? gate->stride_h : 0;
+}
+
+attn_status launch_slice(Prepared& pr, int slice) {
+  krea::AttnParams& p = pr.p;
+  p.q_begin = slice * pr.chunk;
+  p.q_end = std::min(pr.length, p.q_begin + pr.chunk);
+  plan_tail(p, krea::attention_items(pr.a, p.q_end - p.q_begin), pr.dp->plan.lay.nb, pr.cus, pr.w.tail_parts);
+  p.item_order = pr.dp->plan.item_order.empty()
+                     ? nullptr
+                     : (const int32_t*)(pr.dp->dmem + pr.dp->order_off) + pr.dp->plan.slice_begin[slice];
+  return hip_check(krea::launch_attention(p, pr.a.mode, pr.bf16, pr.st), "attention launch");
+}
+
+attn_status forward_impl(const attn_args* args, const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                         const attn_tensor* gate, const attn_tensor* o, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  Prepared pr;
+  attn_status s = prepare(args, q, k, v, gate, o, workspace, workspace_bytes, stream, &pr);
+  if (s != ATTN_OK) return s;
+  if (g_ev_start && (s = hip_check(hipEventRecord(g_ev_start, pr.st), "timing event")) != ATTN_OK) return s;
+  for (int slice = 0; slice < pr.slices(); ++slice)
+    if ((s = launch_slice(pr, slice)) != ATTN_OK) return s;
+  if (g_ev_stop && (s = hip_check(hipEventRecord(g_ev_stop, pr.st), "timing event")) != ATTN_OK) return s;
   g_err.clear();
   return ATTN_OK;
+}
+
+// Workspace of the block path (bytes from its start, 256-byte aligned regions).
+struct BlockLayout {
+  size_t k = 0, v = 0, q = 0, g = 0, o = 0, attn = 0, gemm = 0, total = 0;
+  int64_t slice_rows = 0;  // most token rows of one query slice
+};
+
+BlockLayout block_layout(const attn_args& a) {
+  const krea::Layout l = krea::make_layout(a);
+  const int chunk = a.q_chunk > 0 ? a.q_chunk : l.length;
+  BlockLayout b;
+  b.slice_rows = std::min<int64_t>(l.n, chunk);
+  const size_t kv = (size_t)a.batch * l.n * a.heads_kv * krea::kHeadDim * 2;
+  const size_t qs = (size_t)a.batch * b.slice_rows * a.heads_q * krea::kHeadDim * 2;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  size_t off = 0;
+  b.k = off;    off = up(off + kv);
+  b.v = off;    off = up(off + kv);
+  b.q = off;    off = up(off + qs);
+  b.g = off;    off = up(off + qs);
+  b.o = off;    off = up(off + qs);
+  b.attn = off; off = up(off + krea::workspace_layout(a).total);
+  b.gemm = off; off = up(off + krea::kGemmWorkspace);
+  b.total = off;
+  return b;
+}
+
+// Physical token rows [r0, r1) of the logical query positions [l0, l1): the same range
+// for dense and TileMix; scanline drops the padding, and what remains is contiguous.
+void physical_rows(const krea::Layout& l, int l0, int l1, int64_t* r0, int64_t* r1) {
+  const int ta = std::min(l0, l.text), tb = std::min(l1, l.text);
+  const int ia = std::max(l0, l.t_pad), ib = std::min(l1, l.t_pad + l.image);
+  *r0 = ta < tb ? ta : (ia < ib ? l.text + (ia - l.t_pad) : 0);
+  *r1 = ia < ib ? l.text + (ib - l.t_pad) : (ta < tb ? tb : 0);
+}
+
+attn_status gemm_check(bool ok, const std::string& err) {
+  return ok ? ATTN_OK : fail(ATTN_ERR_DEVICE, err);
 }
 
 }  // namespace
@@ -337,6 +413,98 @@ extern "C" {
 attn_status attn_forward(const attn_args* args, const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
                          const attn_tensor* o, void* workspace, size_t workspace_bytes, void* stream) {
   return forward_impl(args, q, k, v, nullptr, o, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_block_workspace_bytes(const attn_args* args, int32_t model_dim, size_t* bytes) {
+  attn_status s = check_args(args);
+  if (s != ATTN_OK) return s;
+  if (!bytes) return fail(ATTN_ERR_INVALID_ARG, "bytes is NULL");
+  if (model_dim <= 0 || model_dim % 8) return fail(ATTN_ERR_INVALID_ARG, "model_dim must be a positive multiple of 8");
+  *bytes = block_layout(*args).total;
+  g_err.clear();
+  return ATTN_OK;
+}
+
+attn_status attn_block_forward(const attn_args* args, const attn_block_weights* wt, const void* x, void* y,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  attn_status s = check_args(args);
+  if (s != ATTN_OK) return s;
+  if (!wt || !wt->w_q || !wt->w_k || !wt->w_v || !wt->w_gate || !wt->w_o)
+    return fail(ATTN_ERR_INVALID_ARG, "block weights missing");
+  if (wt->model_dim <= 0 || wt->model_dim % 8 || wt->reserved != 0)
+    return fail(ATTN_ERR_INVALID_ARG, "model_dim must be a positive multiple of 8 and reserved 0");
+  const void* ptrs[] = {wt->w_q, wt->w_k, wt->w_v, wt->w_gate, wt->w_o, x, y};
+  for (const void* ptr : ptrs)
+    if (!ptr || ((uintptr_t)ptr & 15)) return fail(ATTN_ERR_INVALID_ARG, "x, y and weights must be 16-byte aligned");
+  const attn_args& a = *args;
+  const BlockLayout bl = block_layout(a);
+  if (!workspace || workspace_bytes < bl.total)
+    return fail(ATTN_ERR_WORKSPACE, "workspace smaller than attn_block_workspace_bytes()");
+  if ((uintptr_t)workspace & 255) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const krea::Layout lay = krea::make_layout(a);
+  const bool bf16 = a.dtype == ATTN_BF16;
+  const int64_t D = wt->model_dim, N = lay.n, B = a.batch;
+  const int64_t hq = (int64_t)a.heads_q * krea::kHeadDim, hkv = (int64_t)a.heads_kv * krea::kHeadDim;
+  unsigned char* ws = (unsigned char*)workspace;
+  void* kbuf = ws + bl.k;
+  void* vbuf = ws + bl.v;
+  uint16_t* qbuf = (uint16_t*)(ws + bl.q);
+  uint16_t* gbuf = (uint16_t*)(ws + bl.g);
+  uint16_t* obuf = (uint16_t*)(ws + bl.o);
+  void* gws = ws + bl.gemm;
+  hipStream_t st = (hipStream_t)stream;
+  std::string err;
+  // pass one: K and V of every token
+  if ((s = gemm_check(krea::gemm_rows(bf16, N, hkv, D, x, D, N * D, wt->w_k, kbuf, hkv, N * hkv, (int)B, false, gws,
+                                      krea::kGemmWorkspace, st, &err),
+                      err)) ||
+      (s = gemm_check(krea::gemm_rows(bf16, N, hkv, D, x, D, N * D, wt->w_v, vbuf, hkv, N * hkv, (int)B, false, gws,
+                                      krea::kGemmWorkspace, st, &err),
+                      err)))
+    return s;
+  const attn_tensor kt{kbuf, N * hkv, hkv, krea::kHeadDim};
+  const attn_tensor vt{vbuf, N * hkv, hkv, krea::kHeadDim};
+  // the slice buffers hold the slice's rows only: a tensor view whose token r0 is the
+  // buffer's first row (rows outside the slice are never touched)
+  auto view = [&](uint16_t* buf, int64_t r0, int64_t rows) {
+    return attn_tensor{buf - r0 * hq, rows * hq, hq, krea::kHeadDim};
+  };
+  int64_t r0 = 0, r1 = 0;
+  const int chunk = a.q_chunk > 0 ? a.q_chunk : lay.length;
+  physical_rows(lay, 0, std::min(lay.length, chunk), &r0, &r1);
+  attn_tensor qv = view(qbuf, r0, std::max<int64_t>(r1 - r0, 1)), gv = view(gbuf, r0, std::max<int64_t>(r1 - r0, 1)),
+              ov = view(obuf, r0, std::max<int64_t>(r1 - r0, 1));
+  Prepared pr;
+  if ((s = prepare(args, &qv, &kt, &vt, &gv, &ov, ws + bl.attn, krea::workspace_layout(a).total, stream, &pr)) !=
+      ATTN_OK)
+    return s;
+  // pass two, one query slice at a time
+  for (int slice = 0; slice < pr.slices(); ++slice) {
+    const int l0 = slice * pr.chunk;
+    physical_rows(lay, l0, std::min(pr.length, l0 + pr.chunk), &r0, &r1);
+    const int64_t rows = r1 - r0;
+    if (rows <= 0) continue;
+    const uint16_t* xs = (const uint16_t*)x + r0 * D;
+    if ((s = gemm_check(krea::gemm_rows(bf16, rows, hq, D, xs, D, N * D, wt->w_q, qbuf, hq, rows * hq, (int)B, false,
+                                        gws, krea::kGemmWorkspace, st, &err),
+                        err)) ||
+        (s = gemm_check(krea::gemm_rows(bf16, rows, hq, D, xs, D, N * D, wt->w_gate, gbuf, hq, rows * hq, (int)B,
+                                        false, gws, krea::kGemmWorkspace, st, &err),
+                        err)))
+      return s;
+    qv = view(qbuf, r0, rows);
+    gv = view(gbuf, r0, rows);
+    ov = view(obuf, r0, rows);
+    pr.p.q = ref(&qv);
+    set_output(pr.p, &ov, &gv);
+    if ((s = launch_slice(pr, slice)) != ATTN_OK) return s;
+    if ((s = gemm_check(krea::gemm_rows(bf16, rows, D, hq, obuf, hq, rows * hq, wt->w_o, (uint16_t*)y + r0 * D, D,
+                                        N * D, (int)B, true, gws, krea::kGemmWorkspace, st, &err),
+                        err)))
+      return s;
+  }
+  g_err.clear();
+  return ATTN_OK;
 }
 
 attn_status attn_forward_gated(const attn_args* args, const attn_tensor* q, const attn_tensor* k,

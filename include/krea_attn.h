@@ -138,6 +138,42 @@ attn_status attn_forward_gated(const attn_args* args, const attn_tensor* q, cons
                                const attn_tensor* v, const attn_tensor* gate, const attn_tensor* o,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Weights of one block's attention context, device pointers in the args dtype, each a
+ * row-major [in][out] matrix applied to token rows as x W:
+ * w_q and w_gate [D][Hq * 128], w_k and w_v [D][Hkv * 128], w_o [Hq * 128][D]. */
+typedef struct {
+  const void* w_q;
+  const void* w_k;
+  const void* w_v;
+  const void* w_gate;
+  const void* w_o;
+  int32_t model_dim; /* D, a multiple of 8 */
+  int32_t reserved;  /* 0 */
+} attn_block_weights;
+
+/* Bytes of device workspace attn_block_forward needs: K and V of every token, q, gate and
+ * gated attention output of one query slice, attn_forward's workspace, and the GEMM
+ * library's.  Host only. */
+attn_status attn_block_workspace_bytes(const attn_args* args, int32_t model_dim, size_t* bytes);
+
+/* The attention context of one block, in the two passes of "LayerStream: Krea2 Chunking"
+ * ("What the node does to the block"):
+ *   pass one:  K = x W_k and V = x W_v for every token;
+ *   pass two:  for each slice of q_chunk query positions (all of them when q_chunk is 0):
+ *              q = x W_q and g = x W_gate for the slice's tokens, o = attention of the slice
+ *              against the full K/V with o * sigmoid(g) applied in the store (the kernels
+ *              of attn_forward_gated), then y[slice] += o W_o.
+ * x: [B, N, D] and y: [B, N, D], contiguous device arrays in the args dtype (16-byte
+ * aligned); x is read, y is added into in place (the residual stream).  The projections
+ * are plain GEMMs on hipBLASLt with fp32 accumulation and outputs in the args dtype.
+ * Every mode of attn_forward applies.  Enqueued on `stream`; the library keeps one
+ * hipBLASLt handle per device for the process' lifetime.  Errors: those of attn_forward;
+ * weights or x or y NULL or misaligned, model_dim not a positive multiple of 8 or
+ * reserved not 0 give ATTN_ERR_INVALID_ARG; a GEMM the library cannot run gives
+ * ATTN_ERR_DEVICE. */
+attn_status attn_block_forward(const attn_args* args, const attn_block_weights* weights, const void* x, void* y,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Host-only plan exports (no GPU needed). */
 attn_status attn_plan_info_get(const attn_args* args, attn_plan_info* out);
 /* TileMix route map, row-major uint8 [nb][nb] over (query block, key block): 0 FP16, 1 INT8. */

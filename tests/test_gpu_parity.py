@@ -345,3 +345,65 @@ def test_int8_baseline_on_text_outliers(dev):
         rel[pattern] = float(np.sqrt(np.mean((got - exact) ** 2) / np.mean(exact ** 2)))
     print("rel RMS error against exact attention:", rel)
     assert rel["all"] > 10.0 * rel["band"]
+
+
+# ----------------------------------------------------------------------------- block context
+BLOCK = [
+    ("dense", _w(heads_q=8, heads_kv=2), 256),
+    ("dense_sliced", _w(heads_q=8, heads_kv=2, q_chunk=128), 256),
+    ("tilemix_sliced", _w(heads_q=8, heads_kv=2, mode="tilemix", pattern="band", percentage=0.6, band_blocks=0,
+                          smooth_k=True, text_tokens=130, img_rows=12, img_cols=40, q_chunk=256), 512),
+    ("scanline_sliced", _w(heads_q=4, heads_kv=1, mode="scanline", window=3, tile_aligned=False, text_tokens=77,
+                           q_chunk=128), 128),
+    ("dense_f16_b2", _w(dtype="f16", batch=2, heads_q=4, heads_kv=1, text_tokens=64, img_rows=9, img_cols=21), 192),
+]
+
+
+def _block_run(w, d_model, dev, y0_zero=True, seed=5):
+    from synth import make_block_inputs
+    x, wq, wk, wv, wg, wo, y0 = make_block_inputs(w, d_model, seed)
+    if y0_zero:
+        y0 = torch.zeros_like(y0)
+    y = y0.clone().to(dev)
+    ka.block_forward(*(t.to(dev) for t in (x, wq, wk, wv, wg, wo)), y, heads_q=w.heads_q, heads_kv=w.heads_kv,
+                     **_kw(w))
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64), (x, wq, wk, wv, wg, wo, y0)
+
+
+@pytest.mark.parametrize("name,w,d_model", BLOCK, ids=[n for n, _, _ in BLOCK])
+def test_block_vs_oracle(dev, name, w, d_model):
+    """attn_block_forward (K/V for every token, then per slice q, gate, gated attention and
+    the output projection added into y) against the fp64 block oracle, y0 = 0."""
+    got, ins = _block_run(w, d_model, dev)
+    ref = block_ref.block_context(*(to_f64(t) for t in ins), w)
+    mx, mn, rel = _assert_close(got, ref, name)
+    print(f"block {name}: max {mx:.2e} mean {mn:.2e} rel {rel:.2e}")
+
+
+def test_block_adds_into_y(dev):
+    """y is the residual: the call adds the context into it (one rounding of the sum)."""
+    w = _w(heads_q=8, heads_kv=2)
+    delta, _ = _block_run(w, 256, dev)
+    got, ins = _block_run(w, 256, dev, y0_zero=False)
+    y0 = to_f64(ins[-1])
+    want = y0 + delta
+    # The GPU rounds y0 + c once to bf16 (c the fp32 context); delta = bf16(c).  So
+    # |got - want| <= u |y0 + c| + u |c| <= u (|y0| + 2 |c|), u = 2^-8 the bf16 unit
+    # roundoff (plus the fp32 difference between the two GEMM runs).
+    bound = 2.0 ** -8 * (np.abs(y0) + 2.0 * np.abs(delta)) * 1.01 + 1e-6
+    ratio = np.abs(got - want) / bound
+    i = np.unravel_index(np.argmax(ratio), ratio.shape)
+    assert ratio.max() <= 1.0, (ratio.max(), got[i], want[i], y0[i], delta[i])
+
+
+def test_block_krea_1mp_sampled(dev):
+    """The Krea 2 block at 1 MP (D = 6144, 48 / 12 heads, 4096-token query slices, the
+    chunking node's default) against the oracle on sampled rows of every slice."""
+    w = WORKLOADS["1mp_dense"].with_(q_chunk=4096)
+    got, ins = _block_run(w, 6144, dev, seed=21)
+    ora = block_ref.BlockOracle(*(to_f64(t) for t in ins), w)
+    rows = np.array([0, 511, 512, 2047, 4095, 4096, 4607])
+    ref = ora.rows(0, rows)
+    mx, mn, rel = _assert_close(got[0, rows], ref, "block 1mp")
+    print(f"block 1mp sampled: max {mx:.2e} mean {mn:.2e} rel {rel:.2e}")

@@ -46,7 +46,7 @@ def test_struct_layout_matches_header(tmp_path):
         pytest.skip("no C compiler")
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "krea_attn.h"', "int main(void) {"]
     for struct, cls in (("attn_args", ka.AttnArgs), ("attn_tensor", ka.AttnTensor),
-                        ("attn_plan_info", ka.AttnPlanInfo)):
+                        ("attn_plan_info", ka.AttnPlanInfo), ("attn_block_weights", ka.AttnBlockWeights)):
         lines.append(f'printf("{struct} %zu\\n", sizeof({struct}));')
         for f, _ in cls._fields_:
             lines.append(f'printf("{struct}.{f} %zu\\n", offsetof({struct}, {f}));')
@@ -58,7 +58,7 @@ def test_struct_layout_matches_header(tmp_path):
     got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True,
                                                   check=True).stdout.splitlines())
     for struct, cls in (("attn_args", ka.AttnArgs), ("attn_tensor", ka.AttnTensor),
-                        ("attn_plan_info", ka.AttnPlanInfo)):
+                        ("attn_plan_info", ka.AttnPlanInfo), ("attn_block_weights", ka.AttnBlockWeights)):
         assert int(got[struct]) == ctypes.sizeof(cls)
         for f, _ in cls._fields_:
             assert int(got[f"{struct}.{f}"]) == getattr(cls, f).offset, (struct, f)
@@ -190,6 +190,21 @@ def test_workspace_sizes(lib):
     n = ka.workspace_bytes(tm)
     # plus at least the INT8 K codes: 12 KV heads x 36 blocks x 128 x 128
     assert n >= dense + 12 * 36 * 128 * 128
+
+
+def test_block_workspace_and_validation(lib):
+    """attn_block_workspace_bytes: K, V of every token, q / gate / output of one query slice,
+    the attention workspace and 32 MiB for the GEMM library; bad model dims are refused."""
+    args = ka.make_args(text_tokens=512, img_rows=64, img_cols=64, q_chunk=1024)
+    n, hq, hkv = 4608, 48 * 128, 12 * 128
+    want = (_a256(n * hkv * 2) * 2 + _a256(1024 * hq * 2) * 3 + _a256(ka.workspace_bytes(args))
+            + (32 << 20))
+    assert ka.block_workspace_bytes(args, 6144) == want
+    out = ctypes.c_size_t()
+    assert lib.attn_block_workspace_bytes(ctypes.byref(args), 6150, ctypes.byref(out)) == -1
+    assert lib.attn_block_workspace_bytes(ctypes.byref(args), 0, ctypes.byref(out)) == -1
+    weights = ka.AttnBlockWeights(None, None, None, None, None, 6144, 0)
+    assert lib.attn_block_forward(ctypes.byref(args), ctypes.byref(weights), None, None, None, 0, None) == -1
 
 
 def _status(fn, *a):
