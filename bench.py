@@ -11,7 +11,8 @@ milliseconds of work after an idle period run up to ~10 % slower.
 
 value = effective TFLOP/s = 4 * Hq * N^2 * d / time per call (dense-equivalent flops).
 roofline: the attention kernel's algorithmic flops per launch / its mean launch duration
-(HIP events on the stream the kernel runs on), against MI355X's dense bf16 MFMA peak.
+(HIP events on the stream the kernel runs on), against MI355X's dense bf16 MFMA peak; also
+against the rate the library's MFMA probe sustains on the same GPU (measured_mfma_peak).
 cpu_baseline: the fp64 numpy oracle on a bounded sample of the same workload (a few
 query heads), timed on this host's cores, scaled to TFLOP/s.
 detail: the same timing for the other Krea workloads (1 MP TileMix band, 1 MP scanline,
@@ -196,6 +197,11 @@ class _HipRuntime:
             raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
         return ev
 
+    def record(self, ev, stream):
+        rc = self.lib.hipEventRecord(ev, self.c.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
     def elapsed_ms(self, a, b):
         ms = self.c.c_float()
         rc = self.lib.hipEventElapsedTime(self.c.byref(ms), a, b)
@@ -241,6 +247,31 @@ def attention_kernel_time(name, steps, warmup, dev):
         hip.destroy(a)
         hip.destroy(b)
     return total / steps
+
+
+def mfma_peak(dev, kind, iters=20000, launches=5):
+    """Sustained MFMA rate (TFLOP/s or TOPS) of the 32x32 product the attention kernel uses,
+    from the library's probe (attn_mfma_probe): two 8-wave workgroups per CU, each wave
+    issuing four independent accumulation chains; timed with the same fence-free events."""
+    import torch
+
+    import diffusion_transformer_attention_bidirectional_amd as ka
+
+    wgs = 2 * torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ka.mfma_probe(kind, wgs, iters, sink)  # untimed: clocks up, code resident
+    hip = _HipRuntime()
+    a, b = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    hip.record(a, stream)
+    ops = sum(ka.mfma_probe(kind, wgs, iters, sink) for _ in range(launches))
+    hip.record(b, stream)
+    torch.cuda.synchronize()
+    ms = hip.elapsed_ms(a, b)
+    hip.destroy(a)
+    hip.destroy(b)
+    return ops / (ms * 1e-3) / 1e12
 
 
 def copy_reference(dev, nbytes=1 << 30, launches=5):
@@ -343,6 +374,9 @@ def main():
     kern_ms = attention_kernel_time(a.workload, a.steps, a.warmup, dev)
     achieved = (head["bf16_flops"] + head["int8_ops"]) / (kern_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if head["int8_ops"] == 0 else roofline_peak_mixed(head["bf16_flops"], head["int8_ops"])
+    measured = {k: mfma_peak(dev, k) for k in ("bf16", "i8")}
+    print(f"# MFMA probe: bf16 {measured['bf16']:.0f} TFLOP/s, i8 {measured['i8']:.0f} TOPS sustained",
+          file=sys.stderr, flush=True)
     detail = {}
     if not a.no_detail:
         for name in DETAIL:
@@ -389,7 +423,13 @@ def main():
                    "tokens": w.tokens, "mode": w.mode, "q_chunk": w.q_chunk},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": measured_traffic(a.workload),
-                     "kernel": f"attn_fwd_kernel<bf16, {w.mode}>", "kernel_ms": round(kern_ms, 5)},
+                     "kernel": f"attn_fwd_kernel<bf16, {w.mode}>", "kernel_ms": round(kern_ms, 5),
+                     # the same kernel against the rate the MFMA probe sustains on this GPU
+                     "measured_mfma_peak": {"bf16_tflops": round(measured["bf16"], 1),
+                                            "i8_tops": round(measured["i8"], 1)},
+                     "frac_of_measured_peak": round(
+                         (head["bf16_flops"] / measured["bf16"] + head["int8_ops"] / measured["i8"]) / 1e12
+                         / (kern_ms * 1e-3), 4)},
         "cpu_baseline": None if cpu is None else {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
         "detail": detail,
     }

@@ -31,7 +31,7 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported dtype", -3: "unsuppo
 EXPORTS = ("attn_workspace_bytes", "attn_forward", "attn_forward_gated", "attn_block_workspace_bytes",
            "attn_block_forward", "attn_plan_info_get", "attn_route_map",
            "attn_block_mask", "attn_item_order", "attn_quantize", "attn_int8_scores", "attn_mask_row_counts",
-           "attn_set_kernel_events", "attn_status_string", "attn_last_error")
+           "attn_mfma_probe", "attn_set_kernel_events", "attn_status_string", "attn_last_error")
 
 
 class KreaAttnError(RuntimeError):
@@ -101,6 +101,7 @@ def load_library(path: str = LIB_PATH):
         "attn_quantize": [P(AttnArgs), P(AttnTensor), P(AttnTensor), vp, sz, vp, vp, vp, vp, vp, vp],
         "attn_int8_scores": [P(AttnArgs), P(AttnTensor), P(AttnTensor), vp, sz, vp, i32, vp, vp],
         "attn_mask_row_counts": [P(AttnArgs), vp, vp],
+        "attn_mfma_probe": [i32, i32, i32, vp, P(ctypes.c_int64), vp],
         "attn_set_kernel_events": [vp, vp],
     }
     for name, argtypes in sig.items():
@@ -224,6 +225,20 @@ def block_forward(x, wq, wk, wv, wg, wo, y, *, text_tokens, img_rows=0, img_cols
                                              ctypes.c_void_p(y.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
                                              workspace.numel(), _stream_handle(stream, x.device)))
     return y
+
+
+PROBE_KINDS = {"bf16": 0, "f16": 1, "i8": 2}
+
+
+def mfma_probe(kind: str, workgroups: int, iters: int, sink, stream=None) -> int:
+    """Enqueue one MFMA throughput probe launch (attn_mfma_probe) on the stream; returns
+    the operations it performs.  sink: a device tensor of at least 4 bytes, which receives a
+    checksum of the first wave's accumulators."""
+    ops = ctypes.c_int64(0)
+    _check(load_library().attn_mfma_probe(PROBE_KINDS[kind], int(workgroups), int(iters),
+                                          ctypes.c_void_p(sink.data_ptr()), ctypes.byref(ops),
+                                          _stream_handle(stream, sink.device)))
+    return ops.value
 
 
 def set_kernel_events(start=None, stop=None):

@@ -635,6 +635,20 @@ attn_status attn_mask_row_counts(const attn_args* args, int32_t* out, void* stre
   return ATTN_OK;
 }
 
+attn_status attn_mfma_probe(int32_t kind, int32_t workgroups, int32_t iters, void* sink, int64_t* ops,
+                            void* stream) {
+  if (kind < ATTN_PROBE_BF16 || kind > ATTN_PROBE_I8) return fail(ATTN_ERR_INVALID_ARG, "unknown probe kind");
+  if (workgroups < 1 || iters < 1) return fail(ATTN_ERR_INVALID_ARG, "workgroups and iters must be >= 1");
+  if (sink == nullptr || ops == nullptr) return fail(ATTN_ERR_INVALID_ARG, "sink and ops must not be NULL");
+  const int64_t per_mfma = kind == ATTN_PROBE_I8 ? 2LL * 32 * 32 * 32 : 2LL * 32 * 32 * 16;
+  *ops = per_mfma * 4 * (int64_t)iters * 8 * (int64_t)workgroups;
+  attn_status s;
+  if ((s = hip_check(krea::launch_mfma_probe(kind, workgroups, iters, (float*)sink, (hipStream_t)stream), "launch")))
+    return s;
+  g_err.clear();
+  return ATTN_OK;
+}
+
 attn_status attn_set_kernel_events(void* start_event, void* stop_event) {
   if ((start_event == nullptr) != (stop_event == nullptr))
     return fail(ATTN_ERR_INVALID_ARG, "give both events or neither");

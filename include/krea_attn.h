@@ -220,6 +220,21 @@ attn_status attn_mask_row_counts(const attn_args* args, int32_t* out, void* stre
  * return ATTN_ERR_DEVICE.  Host only; enqueues nothing by itself. */
 attn_status attn_set_kernel_events(void* start_event, void* stop_event);
 
+/* MFMA throughput probe (measurement only; no attention work).  Enqueues one launch of
+ * `workgroups` workgroups of 8 waves, the attention kernel's occupancy.  Each wave issues
+ * 4 * iters independent MFMAs of `kind`:
+ *   ATTN_PROBE_BF16, ATTN_PROBE_F16: 32x32x16 with fp32 accumulation;
+ *   ATTN_PROBE_I8: 32x32x32 with int32 accumulation.
+ * Timing the launch gives the rate the chip sustains for the products the attention
+ * kernel is built from, to set beside the published dense peak.
+ * - *ops (host pointer) receives the operations the launch performs (2 per multiply-add).
+ * - sink: device memory of at least 4 bytes; receives a 32-bit checksum of the first
+ *   wave's accumulators (the same for the same kind and iters).
+ * workgroups >= 1 and iters >= 1; anything else is ATTN_ERR_INVALID_ARG.  Async on stream. */
+enum { ATTN_PROBE_BF16 = 0, ATTN_PROBE_F16 = 1, ATTN_PROBE_I8 = 2 };
+attn_status attn_mfma_probe(int32_t kind, int32_t workgroups, int32_t iters, void* sink, int64_t* ops,
+                            void* stream);
+
 const char* attn_status_string(attn_status status);
 /* Message for the last error on the calling thread ("" if none). */
 const char* attn_last_error(void);

@@ -407,3 +407,18 @@ def test_block_krea_1mp_sampled(dev):
     ref = ora.rows(0, rows)
     mx, mn, rel = _assert_close(got[0, rows], ref, "block 1mp")
     print(f"block 1mp sampled: max {mx:.2e} mean {mn:.2e} rel {rel:.2e}")
+
+
+@pytest.mark.parametrize("kind,per", [("bf16", 2 * 32 * 32 * 16), ("f16", 2 * 32 * 32 * 16), ("i8", 2 * 32 * 32 * 32)])
+def test_mfma_probe_runs_and_counts(dev, kind, per):
+    """The MFMA throughput probe reports the operations of 4 * iters products per wave of 8
+    waves per workgroup, and its products run: the accumulator checksum changes with iters
+    and repeats exactly for the same iters."""
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    sums = []
+    for iters in (1, 2, 2):
+        ops = ka.mfma_probe(kind, 4, iters, sink)
+        torch.cuda.synchronize()
+        assert ops == per * 4 * iters * 8 * 4
+        sums.append(sink.item())
+    assert sums[0] != sums[1] and sums[1] == sums[2]

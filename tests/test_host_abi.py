@@ -284,6 +284,19 @@ def test_route_and_mask_reject_wrong_mode(lib):
     assert lib.attn_route_map(ctypes.byref(tm), out.ctypes.data, 35) == -1
 
 
+def test_mfma_probe_validation(lib):
+    """The probe rejects bad arguments before any device work (no GPU needed)."""
+    ops = ctypes.c_int64(-7)
+    sink = ctypes.c_void_p(0x100000)
+    assert lib.attn_mfma_probe(3, 1, 1, sink, ctypes.byref(ops), None) == -1
+    assert lib.attn_mfma_probe(-1, 1, 1, sink, ctypes.byref(ops), None) == -1
+    assert lib.attn_mfma_probe(0, 0, 1, sink, ctypes.byref(ops), None) == -1
+    assert lib.attn_mfma_probe(0, 1, 0, sink, ctypes.byref(ops), None) == -1
+    assert lib.attn_mfma_probe(0, 1, 1, None, ctypes.byref(ops), None) == -1
+    assert lib.attn_mfma_probe(0, 1, 1, sink, None, None) == -1
+    assert ops.value == -7
+
+
 def test_status_strings(lib):
     for code, text in ka.STATUS.items():
         assert lib.attn_status_string(code).decode() == text
