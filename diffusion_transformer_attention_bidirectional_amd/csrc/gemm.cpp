@@ -16,8 +16,11 @@ namespace {
 std::mutex g_mu;
 std::map<int, hipblasLtHandle_t> g_handles;  // one per device, for the process' lifetime
 
-using AlgoKey = std::tuple<int, bool, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int, bool>;
-std::map<AlgoKey, hipblasLtMatmulAlgo_t> g_algos;  // the heuristic's first choice per shape
+// device, dtype, shape, strides, batch, accumulate, workspace bytes: an algorithm chosen
+// under a larger workspace may need more than a later call provides
+using AlgoKey =
+    std::tuple<int, bool, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int, bool, size_t>;
+std::map<AlgoKey, hipblasLtMatmulAlgo_t> g_algos;  // the heuristic's first choice per call shape
 
 bool check(hipblasStatus_t s, const char* what, std::string* err) {
   if (s == HIPBLAS_STATUS_SUCCESS) return true;
@@ -84,7 +87,7 @@ bool gemm_rows(bool bf16, int64_t M, int64_t N, int64_t K, const void* X, int64_
       !check(hipblasLtMatrixLayoutCreate(&d.c, dt, N, M, ldy), "layout Y", err) || !batched(d.a, batch, 0, err) ||
       !batched(d.b, batch, sx, err) || !batched(d.c, batch, sy, err))
     return false;
-  const AlgoKey key{dev, bf16, M, N, K, ldx, sx, ldy, sy, batch, accumulate};
+  const AlgoKey key{dev, bf16, M, N, K, ldx, sx, ldy, sy, batch, accumulate, workspace_bytes};
   hipblasLtMatmulAlgo_t algo;
   bool have = false;
   {
