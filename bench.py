@@ -360,7 +360,8 @@ def main():
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this attention path is built and measured on a single MI355X "
-              "(see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
+              "(its (batch, KV head) units would shard across GPUs without exchange); run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
     import torch
 
