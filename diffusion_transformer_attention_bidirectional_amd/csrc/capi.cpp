@@ -498,8 +498,11 @@ attn_status attn_block_forward(const attn_args* args, const attn_block_weights* 
     pr.p.q = ref(&qv);
     set_output(pr.p, &ov, &gv);
     if ((s = launch_slice(pr, slice)) != ATTN_OK) return s;
+    // the gate slice has been read by the attention launch: when the projection's output
+    // fits in it, it is where the first call of this shape times the GEMM's candidates
+    void* tune = rows * D <= bl.slice_rows * hq ? (void*)gbuf : nullptr;
     if ((s = gemm_check(krea::gemm_rows(bf16, rows, D, hq, obuf, hq, rows * hq, wt->w_o, (uint16_t*)y + r0 * D, D,
-                                        N * D, (int)B, true, gws, krea::kGemmWorkspace, st, &err),
+                                        N * D, (int)B, true, gws, krea::kGemmWorkspace, st, &err, tune),
                         err)))
       return s;
   }

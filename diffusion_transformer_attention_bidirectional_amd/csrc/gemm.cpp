@@ -52,11 +52,59 @@ bool batched(hipblasLtMatrixLayout_t l, int batch, int64_t stride, std::string* 
                "layout batch stride", err);
 }
 
+// Candidates timed on the first call of a shape, and launches per candidate timing.
+constexpr int kCandidates = 12;
+constexpr int kTimedRuns = 3;
+
+// The fastest of hipBLASLt's candidates for the described product, run with beta = 0 on
+// `out` (laid out as `c`).  Candidates that fail to launch are skipped.
+bool fastest(hipblasLtHandle_t h, const Descs& d, hipblasLtMatrixLayout_t c, const void* W, const void* X,
+             void* out, void* workspace, size_t workspace_bytes, hipStream_t stream,
+             const hipblasLtMatmulHeuristicResult_t* res, int found, hipblasLtMatmulAlgo_t* best,
+             std::string* err) {
+  *best = res[0].algo;
+  if (found < 2) return true;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) hipEventDestroy(e0);
+    if (err) *err = "hipEventCreate failed";
+    return false;
+  }
+  const float alpha = 1.0f, beta = 0.0f;
+  float best_ms = 0.f;
+  bool have = false, ok = true;
+  for (int i = 0; i < found && ok; ++i) {
+    if (res[i].state != HIPBLAS_STATUS_SUCCESS || res[i].workspaceSize > workspace_bytes) continue;
+    auto run = [&]() {
+      return hipblasLtMatmul(h, d.op, &alpha, W, d.a, X, d.b, &beta, out, c, out, c, &res[i].algo, workspace,
+                             workspace_bytes, stream) == HIPBLAS_STATUS_SUCCESS;
+    };
+    if (!run()) continue;  // this candidate does not take these operands
+    bool timed = hipEventRecord(e0, stream) == hipSuccess;
+    for (int r = 0; r < kTimedRuns && timed; ++r) timed = run();
+    timed = timed && hipEventRecord(e1, stream) == hipSuccess && hipEventSynchronize(e1) == hipSuccess;
+    float ms = 0.f;
+    if (!timed || hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+      ok = false;
+      break;
+    }
+    if (!have || ms < best_ms) {
+      best_ms = ms;
+      *best = res[i].algo;
+      have = true;
+    }
+  }
+  hipEventDestroy(e0);
+  hipEventDestroy(e1);
+  if (!ok && err) *err = "timing the hipBLASLt candidates failed";
+  return ok;
+}
+
 }  // namespace
 
 bool gemm_rows(bool bf16, int64_t M, int64_t N, int64_t K, const void* X, int64_t ldx, int64_t sx, const void* W,
                void* Y, int64_t ldy, int64_t sy, int batch, bool accumulate, void* workspace, size_t workspace_bytes,
-               hipStream_t stream, std::string* err) {
+               hipStream_t stream, std::string* err, void* scratch) {
   if (M <= 0 || N <= 0 || K <= 0 || batch <= 0) return true;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
@@ -105,16 +153,28 @@ bool gemm_rows(bool bf16, int64_t M, int64_t N, int64_t K, const void* X, int64_
                                                      sizeof(wsb)),
                "preference workspace", err))
       return false;
-    hipblasLtMatmulHeuristicResult_t res[1];
+    hipblasLtMatmulHeuristicResult_t res[kCandidates];
     int found = 0;
-    if (!check(hipblasLtMatmulAlgoGetHeuristic(h, d.op, d.a, d.b, d.c, d.c, d.pref, 1, res, &found), "heuristic",
-               err))
+    if (!check(hipblasLtMatmulAlgoGetHeuristic(h, d.op, d.a, d.b, d.c, d.c, d.pref, kCandidates, res, &found),
+               "heuristic", err))
       return false;
     if (found < 1) {
       if (err) *err = "hipBLASLt has no algorithm for this GEMM";
       return false;
     }
-    algo = res[0].algo;
+    if (!accumulate) {
+      if (!fastest(h, d, d.c, W, X, Y, workspace, workspace_bytes, stream, res, found, &algo, err)) return false;
+    } else if (scratch != nullptr) {
+      // the same product without accumulation, into a contiguous scratch of Y's shape
+      hipblasLtMatrixLayout_t ct = nullptr;
+      bool ok = check(hipblasLtMatrixLayoutCreate(&ct, dt, N, M, N), "layout scratch", err) &&
+                batched(ct, batch, N * M, err) &&
+                fastest(h, d, ct, W, X, scratch, workspace, workspace_bytes, stream, res, found, &algo, err);
+      if (ct) hipblasLtMatrixLayoutDestroy(ct);
+      if (!ok) return false;
+    } else {
+      algo = res[0].algo;
+    }
     std::lock_guard<std::mutex> lock(g_mu);
     g_algos[key] = algo;
   }

@@ -167,7 +167,10 @@ attn_status attn_block_workspace_bytes(const attn_args* args, int32_t model_dim,
  * aligned); x is read, y is added into in place (the residual stream).  The projections
  * are plain GEMMs on hipBLASLt with fp32 accumulation and outputs in the args dtype.
  * Every mode of attn_forward applies.  Enqueued on `stream`; the library keeps one
- * hipBLASLt handle per device for the process' lifetime.  Errors: those of attn_forward;
+ * hipBLASLt handle per device for the process' lifetime.  The first call of a shape picks
+ * each GEMM's algorithm by timing hipBLASLt's candidates on the stream, so that call waits
+ * for the stream (make one call before capturing the stream into a graph); later calls of
+ * the shape enqueue only.  Errors: those of attn_forward;
  * weights or x or y NULL or misaligned, model_dim not a positive multiple of 8 or
  * reserved not 0 give ATTN_ERR_INVALID_ARG; a GEMM the library cannot run gives
  * ATTN_ERR_DEVICE. */
