@@ -254,9 +254,16 @@ def _sample_rows(n, t, rng, count=48):
     return np.array(sorted(r for r in rows if 0 <= r < n))
 
 
-@pytest.mark.parametrize("name", ["1mp_dense", "1mp_band", "1mp_scanline", "4mp_band", "4mp_dense", "4mp_scanline"])
-def test_krea_shapes_sampled(dev, name):
-    w = WORKLOADS[name]
+@pytest.mark.parametrize("name,dtype", [("1mp_dense", "bf16"), ("1mp_band", "bf16"), ("1mp_scanline", "bf16"),
+                                        ("4mp_band", "bf16"), ("4mp_dense", "bf16"), ("4mp_scanline", "bf16"),
+                                        ("1mp_dense", "f16"), ("1mp_band", "f16")],
+                         ids=["1mp_dense", "1mp_band", "1mp_scanline", "4mp_band", "4mp_dense", "4mp_scanline",
+                              "1mp_dense_f16", "1mp_band_f16"])
+def test_krea_shapes_sampled(dev, name, dtype):
+    """Krea shapes against the oracle on sampled rows of four heads; the fp16 cases run the
+    fp16 instantiations of the kernels at full size (the same seeded values, rounded to
+    fp16)."""
+    w = WORKLOADS[name].with_(dtype=dtype)
     got, (q, k, v) = _run(w, dev)
     ora = attn_ref.Oracle(to_f64(q), to_f64(k), to_f64(v), w)
     rng = np.random.default_rng(3)
@@ -270,8 +277,9 @@ def test_krea_shapes_sampled(dev, name):
     assert np.isfinite(got).all()
 
 
-def test_krea_1mp_quantiser_bit_exact(dev):
-    _quant_check(WORKLOADS["1mp_band"], dev)
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_krea_1mp_quantiser_bit_exact(dev, dtype):
+    _quant_check(WORKLOADS["1mp_band"].with_(dtype=dtype), dev)
 
 
 def test_krea_1mp_scanline_counts(dev):
