@@ -290,6 +290,23 @@ Plan build_plan(const attn_args& a) {
     p.route = build_route_map(a, p.lay, &p.int8_tiles);
     p.active_tiles = (int64_t)nb * nb;
     p.partial_tiles = (p.lay.n % kTile) ? nb : 0;
+    if (p.int8_tiles > 0) {
+      // key order of each query block: its FP16 full tiles, its INT8 full tiles, then the
+      // ragged last block whatever its route (online softmax does not depend on the
+      // order; the kernel runs each kind in a loop of its own)
+      const int nfull = (p.lay.n % kTile) ? nb - 1 : nb;
+      p.full_count.assign(nb, 0);
+      p.cols.reserve((size_t)nb * nb);
+      for (int qa = 0; qa < nb; ++qa) {
+        for (int pass = 0; pass < 2; ++pass)
+          for (int kb = 0; kb < nfull; ++kb)
+            if ((p.route[(size_t)qa * nb + kb] != 0) == (pass == 1)) {
+              p.cols.push_back(kb);
+              if (pass == 0) ++p.full_count[qa];
+            }
+        if (nfull < nb) p.cols.push_back(nb - 1);
+      }
+    }
   } else if (a.mode == ATTN_SCANLINE) {
     p.bmask = build_block_mask(a, p.lay);
     p.row_ptr.assign(nb + 1, 0);

@@ -33,10 +33,13 @@ struct Plan {
   int mode = ATTN_DENSE;
   std::vector<uint8_t> route;    // TileMix [nb * nb], 1 = INT8
   std::vector<uint8_t> bmask;    // scanline [nb * nb], 0 skip / 1 full / 2 partial
-  // Per query block tile list (scanline): entries of block a are
+  // Per query block tile list.  Scanline: entries of block a are
   // cols[row_ptr[a] .. row_ptr[a + 1]), each (key block) | (partial << 16); the
-  // full_count[a] full tiles come first, then the partial ones (online softmax does not
-  // depend on the order, and the kernel runs the two kinds in separate loops).
+  // full_count[a] full tiles come first, then the partial ones.  TileMix with INT8 tiles:
+  // all nb key blocks of block a at cols[a * nb ..], its full_count[a] FP16 full tiles
+  // first, then its INT8 full tiles, then the ragged last block (no row_ptr).  Online
+  // softmax does not depend on the order, and the kernel runs each kind in a loop of its
+  // own.
   std::vector<int32_t> row_ptr;
   std::vector<int32_t> cols;
   std::vector<int32_t> full_count;
