@@ -1067,39 +1067,42 @@ __global__ void __launch_bounds__(256) prepass_kernel(const AttnParams p, uint16
 // valid rows a = max |x|, inv = fp32(127 / a), scale = fp32(a / 127),
 // code = clamp(rint(x * inv), -127, 127).
 
-// smooth_k mean per (batch, KV head, channel): one workgroup per (KV head, batch).
-__global__ void __launch_bounds__(128) k_mean_kernel(const QuantParams p) {
-  const int g = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
-  const int64_t bg = (int64_t)b * p.heads_kv + g;
-  float m32 = 0.f;
-  if (p.smooth_k) {
-    double tot = 0.0;
-#pragma unroll 16
-    for (int j = 0; j < p.nb; ++j) tot = __dadd_rn(tot, p.k_part[(bg * p.nb + j) * 128 + c]);
-    m32 = __double2float_rn(__ddiv_rn(tot, (double)p.n));
-  }
-  p.k_mean[bg * 128 + c] = m32;
-}
-
-// K codes: one workgroup per (batch, KV head, 128-token block), mean from k_mean_kernel.
+// K codes: one workgroup per (batch, KV head, 128-token block).  Every workgroup of a head
+// sums the smooth_k mean itself from the pre-pass's block partials, with the same fp64 adds
+// in block order (so they all get the same value), while its tile's loads are in flight;
+// the head's first block stores it for the attention kernel.
 template <bool BF16>
 __global__ void __launch_bounds__(256) k_quant_kernel(const QuantParams p) {
   __shared__ float mean[128];
   __shared__ float red[4];
   const int blk = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int64_t bg = (int64_t)b * p.heads_kv + g;
-  if (tid < 128) mean[tid] = p.k_mean[bg * 128 + tid];
-  __syncthreads();
   const int c8 = (tid & 15) * 8;
   const uint16_t* src = (const uint16_t*)p.k.ptr + (int64_t)b * p.k.sb + (int64_t)g * p.k.sh + c8;
+  uint4 raw[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int t = blk * 128 + (tid >> 4) + 16 * i;
+    raw[i] = t < p.n ? *(const uint4*)(src + (int64_t)t * p.k.st) : make_uint4(0, 0, 0, 0);
+  }
+  if (tid < 128) {
+    float m32 = 0.f;
+    if (p.smooth_k) {
+      double tot = 0.0;
+#pragma unroll 16
+      for (int j = 0; j < p.nb; ++j) tot = __dadd_rn(tot, p.k_part[(bg * p.nb + j) * 128 + tid]);
+      m32 = __double2float_rn(__ddiv_rn(tot, (double)p.n));
+    }
+    mean[tid] = m32;
+    if (blk == 0) p.k_mean[bg * 128 + tid] = m32;
+  }
+  __syncthreads();
   float x[8][8];
   float a = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int t = blk * 128 + (tid >> 4) + 16 * i;
-    uint4 raw = make_uint4(0, 0, 0, 0);
-    if (t < p.n) raw = *(const uint4*)(src + (int64_t)t * p.k.st);
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint16_t bits = (e & 1) ? (uint16_t)(w[e >> 1] >> 16) : (uint16_t)(w[e >> 1] & 0xffff);
@@ -1220,7 +1223,6 @@ __global__ void __launch_bounds__(256) mask_counts_kernel(const AttnParams p, in
 
 // ---------------------------------------------------------------- launchers
 hipError_t launch_quant_finish(const QuantParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(k_mean_kernel, dim3(p.heads_kv, p.batch), dim3(128), 0, s, p);
   const dim3 gk(p.nb, p.heads_kv, p.batch);
   if (p.bf16) hipLaunchKernelGGL(k_quant_kernel<true>, gk, dim3(256), 0, s, p);
   else hipLaunchKernelGGL(k_quant_kernel<false>, gk, dim3(256), 0, s, p);
