@@ -1067,11 +1067,33 @@ __global__ void __launch_bounds__(256) prepass_kernel(const AttnParams p, uint16
 // valid rows a = max |x|, inv = fp32(127 / a), scale = fp32(a / 127),
 // code = clamp(rint(x * inv), -127, 127).
 
-// K codes: one workgroup per (batch, KV head, 128-token block).  Every workgroup of a head
-// sums the smooth_k mean itself from the pre-pass's block partials, with the same fp64 adds
-// in block order (so they all get the same value), while its tile's loads are in flight;
-// the head's first block stores it for the attention kernel.
-template <bool BF16>
+// smooth_k mean per (batch, KV head, channel) from the pre-pass's block partials: fp64 adds
+// in block order, then one division by N rounded to fp32.  One thread per channel.
+__device__ __forceinline__ float k_mean_of(const QuantParams& p, int64_t bg, int c) {
+  if (!p.smooth_k) return 0.f;
+  double tot = 0.0;
+#pragma unroll 16
+  for (int j = 0; j < p.nb; ++j) tot = __dadd_rn(tot, p.k_part[(bg * p.nb + j) * 128 + c]);
+  return __double2float_rn(__ddiv_rn(tot, (double)p.n));
+}
+
+// The mean on its own: one workgroup per (KV head, batch), for long sequences, where the
+// serial sum would hold up every quantiser workgroup.
+__global__ void __launch_bounds__(128) k_mean_kernel(const QuantParams p) {
+  const int64_t bg = (int64_t)blockIdx.y * p.heads_kv + blockIdx.x;
+  p.k_mean[bg * 128 + threadIdx.x] = k_mean_of(p, bg, threadIdx.x);
+}
+
+// Heads of at most this many 128-token blocks have their mean summed by the quantiser
+// itself (measured: a separate mean kernel costs 4-5 us of launch and latency at 36 blocks;
+// at 132 blocks the sum in every quantiser workgroup costs 7 us more than that kernel).
+constexpr int kFuseMeanMaxBlocks = 64;
+
+// K codes: one workgroup per (batch, KV head, 128-token block).  FUSED_MEAN: every
+// workgroup of a head sums the smooth_k mean itself (the same adds in the same order, so
+// they all get the same value) while its tile's loads are in flight, and the head's first
+// block stores it for the attention kernel; otherwise k_mean_kernel ran first.
+template <bool BF16, bool FUSED_MEAN>
 __global__ void __launch_bounds__(256) k_quant_kernel(const QuantParams p) {
   __shared__ float mean[128];
   __shared__ float red[4];
@@ -1086,15 +1108,9 @@ __global__ void __launch_bounds__(256) k_quant_kernel(const QuantParams p) {
     raw[i] = t < p.n ? *(const uint4*)(src + (int64_t)t * p.k.st) : make_uint4(0, 0, 0, 0);
   }
   if (tid < 128) {
-    float m32 = 0.f;
-    if (p.smooth_k) {
-      double tot = 0.0;
-#pragma unroll 16
-      for (int j = 0; j < p.nb; ++j) tot = __dadd_rn(tot, p.k_part[(bg * p.nb + j) * 128 + tid]);
-      m32 = __double2float_rn(__ddiv_rn(tot, (double)p.n));
-    }
+    const float m32 = FUSED_MEAN ? k_mean_of(p, bg, tid) : p.k_mean[bg * 128 + tid];
     mean[tid] = m32;
-    if (blk == 0) p.k_mean[bg * 128 + tid] = m32;
+    if (FUSED_MEAN && blk == 0) p.k_mean[bg * 128 + tid] = m32;
   }
   __syncthreads();
   float x[8][8];
@@ -1224,8 +1240,14 @@ __global__ void __launch_bounds__(256) mask_counts_kernel(const AttnParams p, in
 // ---------------------------------------------------------------- launchers
 hipError_t launch_quant_finish(const QuantParams& p, hipStream_t s) {
   const dim3 gk(p.nb, p.heads_kv, p.batch);
-  if (p.bf16) hipLaunchKernelGGL(k_quant_kernel<true>, gk, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL(k_quant_kernel<false>, gk, dim3(256), 0, s, p);
+  if (p.nb <= kFuseMeanMaxBlocks) {
+    if (p.bf16) hipLaunchKernelGGL((k_quant_kernel<true, true>), gk, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((k_quant_kernel<false, true>), gk, dim3(256), 0, s, p);
+  } else {
+    hipLaunchKernelGGL(k_mean_kernel, dim3(p.heads_kv, p.batch), dim3(128), 0, s, p);
+    if (p.bf16) hipLaunchKernelGGL((k_quant_kernel<true, false>), gk, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((k_quant_kernel<false, false>), gk, dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 

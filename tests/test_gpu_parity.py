@@ -214,6 +214,14 @@ def test_quantiser_bit_exact_small(dev):
     _quant_check(_w(mode="tilemix", smooth_k=False, dtype="f16", text_tokens=10, img_rows=3, img_cols=50), dev)
 
 
+def test_quantiser_bit_exact_long(dev):
+    """More than 64 blocks per head (here 71): the smooth_k mean comes from its own kernel
+    instead of the quantiser's workgroups; both must give the oracle's bits."""
+    w = _w(mode="tilemix", smooth_k=True, batch=2, text_tokens=77, img_rows=90, img_cols=100)
+    assert (w.tokens + 127) // 128 > 64
+    _quant_check(w, dev)
+
+
 def test_int8_scores_bit_exact(dev):
     w = _w(mode="tilemix", smooth_k=True, text_tokens=130, img_rows=12, img_cols=40)
     q, k, args, q8, k8 = _quant_check(w, dev)
