@@ -36,8 +36,11 @@ struct AttnParams {
   int smooth_k;
   const uint8_t* route;    // TileMix [nb * nb]
   const int32_t* row_ptr;  // scanline tile lists
+  // per query block key lists: scanline [row_ptr[a], row_ptr[a + 1]) entries of
+  // (key block) | (partial << 16); TileMix with INT8 tiles nb key blocks at a * nb,
+  // FP16 full tiles, then INT8 full tiles, then the ragged block (null: key order)
   const int32_t* cols_list;
-  const int32_t* full_count;  // scanline: full tiles at the head of each list
+  const int32_t* full_count;  // leading full tiles of each list (TileMix: FP16 full tiles)
   const int32_t* item_order;  // scanline: work item of each workgroup of this launch
   const float* k_mean;     // [B, Hkv, 128]
   const int8_t* k_codes;   // [B, Hkv, nb, 128, 128]
