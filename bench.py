@@ -290,13 +290,19 @@ def copy_reference(dev, nbytes=1 << 30, launches=5):
 
 
 def kernel_source_digest():
-    """Digest of the attention kernel sources; counter figures taken from another digest are stale."""
+    """Digest of the attention kernel sources' code (comments and whitespace removed, so that
+    only a change that can change the compiled kernels changes it); counter figures taken
+    under another digest are stale."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     for f in ("kernels.hip", "kernels.hpp"):
-        with open(os.path.join(ROOT, "diffusion_transformer_attention_bidirectional_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "diffusion_transformer_attention_bidirectional_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)  # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
