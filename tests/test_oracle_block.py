@@ -139,3 +139,26 @@ def test_sampled_rows_equal_the_whole(mode):
     rows = np.array([0, 5, 99, 100, 129, 250, 299])
     part = ora.rows(0, rows)
     assert np.max(np.abs(part - full[0, rows])) <= 1e-12 * max(1.0, np.max(np.abs(full)))
+
+
+def test_dense_block_equals_torch_composition():
+    """Dense mode against the same algebra built from torch's CPU library routines in fp64:
+    scaled_dot_product_attention on repeat_interleave-expanded K/V (the GQA grouping), a
+    logistic gate and two matrix products -- code the oracle does not share."""
+    torch = pytest.importorskip("torch")
+    w = _w(heads_q=6, heads_kv=2, head_dim=8, text_tokens=9, img_rows=3, img_cols=5, batch=2)
+    dm = 20
+    x, wq, wk, wv, wg, wo, y0 = _inputs(w, d_model=dm, seed=13)
+    got = block_ref.block_context(x, wq, wk, wv, wg, wo, y0, w)
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    X = t(x)
+    b, n = x.shape[0], x.shape[1]
+    d, g = w.head_dim, w.heads_q // w.heads_kv
+    Q = (X @ t(wq)).reshape(b, n, w.heads_q, d).transpose(1, 2)
+    K = (X @ t(wk)).reshape(b, n, w.heads_kv, d).transpose(1, 2).repeat_interleave(g, dim=1)
+    V = (X @ t(wv)).reshape(b, n, w.heads_kv, d).transpose(1, 2).repeat_interleave(g, dim=1)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    O = torch.nn.functional.scaled_dot_product_attention(Q, K, V, scale=scale)  # [b, Hq, n, d]
+    G = torch.sigmoid((X @ t(wg)).reshape(b, n, w.heads_q, d).transpose(1, 2))
+    want = t(y0) + ((O * G).transpose(1, 2).reshape(b, n, -1) @ t(wo))
+    assert np.max(np.abs(got - want.numpy())) <= 1e-12 * max(1.0, float(want.abs().max()))
