@@ -84,6 +84,10 @@ def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise KreaAttnError(f"{path} is missing: build it with __graft_entry__.build() "
                             "or python diffusion_transformer_attention_bidirectional_amd/build.py")
+    # torch first: the library then binds to the HIP runtime (and hipBLASLt) torch brought
+    # in, so device pointers and streams from torch are valid in it.  Loaded before torch,
+    # it would bind to the system copy, and torch would then load a second runtime.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P = ctypes.POINTER
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
