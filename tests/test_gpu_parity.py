@@ -285,6 +285,18 @@ def test_krea_shapes_sampled(dev, name, dtype):
     assert np.isfinite(got).all()
 
 
+def test_krea_1mp_batch2_band_sampled(dev):
+    """Two samples at the 1 MP shape in TileMix band mode: batch strides, the per-sample
+    smooth_k mean and K codes, checked on sampled rows of the second sample."""
+    w = WORKLOADS["1mp_band"].with_(batch=2)
+    got, (q, k, v) = _run(w, dev)
+    ora = attn_ref.Oracle(to_f64(q), to_f64(k), to_f64(v), w)
+    rows = _sample_rows(w.tokens, w.text_tokens, np.random.default_rng(9), count=24)
+    for h in (1, 30):
+        ref = ora.rows(1, h, rows)
+        _assert_close(got[1, rows, h], ref, f"batch 2 head {h}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_krea_1mp_quantiser_bit_exact(dev, dtype):
     _quant_check(WORKLOADS["1mp_band"].with_(dtype=dtype), dev)
