@@ -285,6 +285,17 @@ def test_krea_shapes_sampled(dev, name, dtype):
     assert np.isfinite(got).all()
 
 
+def test_krea_1mp_scanline_exact_rule_sampled(dev):
+    """The 1 MP scanline call without tile alignment: the exact row rule, so image tiles at
+    the window's edge run through the element mask; sampled rows against the oracle."""
+    w = WORKLOADS["1mp_scanline"].with_(tile_aligned=False)
+    got, (q, k, v) = _run(w, dev)
+    ora = attn_ref.Oracle(to_f64(q), to_f64(k), to_f64(v), w)
+    rows = _sample_rows(w.tokens, w.text_tokens, np.random.default_rng(4), count=32)
+    for h in (2, 45):
+        _assert_close(got[0, rows, h], ora.rows(0, h, rows), f"exact rule head {h}")
+
+
 def test_krea_1mp_batch2_band_sampled(dev):
     """Two samples at the 1 MP shape in TileMix band mode: batch strides, the per-sample
     smooth_k mean and K codes, checked on sampled rows of the second sample."""
