@@ -15,8 +15,8 @@ roofline: the attention kernel's algorithmic flops per launch / its mean launch 
 against the rate the library's MFMA probe sustains on the same GPU (measured_mfma_peak).
 cpu_baseline: the fp64 numpy oracle on a bounded sample of the same workload (a few
 query heads), timed on this host's cores, scaled to TFLOP/s.
-detail: the same timing for the other Krea workloads (1 MP TileMix band, 1 MP scanline,
-4 MP TileMix band sliced, 4 MP dense unsliced and sliced, 4 MP scanline), for the
+detail: the same timing for the other Krea workloads (1 MP TileMix band, 1 MP scanline with
+and without tile alignment, 4 MP TileMix band sliced, 4 MP dense unsliced and sliced, 4 MP scanline), for the
 band-vs-dense and 4 MP comparisons; and the block's attention context
 (attn_block_forward: projections, gated attention in 4096-token query slices, output
 projection into the residual) at 1 MP and 4 MP with the Krea 2 width 6144.
@@ -36,7 +36,8 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
 PEAK_I8_TOPS = 5000.0       # MI355X dense int8 MFMA
 HEADLINE = "1mp_dense"
-DETAIL = ["1mp_band", "1mp_scanline", "4mp_dense", "4mp_dense_sliced", "4mp_band", "4mp_scanline"]
+DETAIL = ["1mp_band", "1mp_scanline", "1mp_scanline_exact", "4mp_dense", "4mp_dense_sliced", "4mp_band",
+          "4mp_scanline"]
 
 
 def algorithmic_work(w, info):

@@ -89,6 +89,9 @@ WORKLOADS: Dict[str, Workload] = {
     "4mp_dense_sliced": Workload(name="4mp_dense_sliced", mode="dense", q_chunk=4096, **_KREA_4MP),
     # 4 MP scanline: 128x128 grid, one 128-token tile per grid row, window 11 (+-5 tiles)
     "4mp_scanline": Workload(name="4mp_scanline", mode="scanline", window=11, tile_aligned=True, **_KREA_4MP),
+    # 1 MP scanline with the exact row rule (no tile alignment): partial tiles masked per element
+    "1mp_scanline_exact": Workload(name="1mp_scanline_exact", mode="scanline", window=11,
+                                   tile_aligned=False, **_KREA_1MP),
 }
 
 _TORCH_DTYPE = {"bf16": torch.bfloat16, "f16": torch.float16}
