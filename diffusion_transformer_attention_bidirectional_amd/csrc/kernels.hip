@@ -100,6 +100,7 @@ __device__ __forceinline__ int grid_row(const AttnParams& p, int t) {
 struct QInfo {
   bool valid, text;
   int row;
+  int lo, hi;  // scanline image query: the image keys of rows row -+ half_window are [lo, hi)
 };
 template <int MODE>
 __device__ __forceinline__ QInfo query_info(const AttnParams& p, int t) {
@@ -107,6 +108,9 @@ __device__ __forceinline__ QInfo query_info(const AttnParams& p, int t) {
   qi.valid = t < p.q_end && tok_valid<MODE>(p, t);
   qi.text = t < p.text;
   qi.row = (MODE == kModeScan && qi.valid && !qi.text) ? grid_row(p, t) : -1;
+  const int rows = p.cols > 0 ? p.image / p.cols : 0;
+  qi.lo = p.t_pad + max(0, qi.row - p.half_window) * p.cols;
+  qi.hi = p.t_pad + (min(rows - 1, qi.row + p.half_window) + 1) * p.cols;
   return qi;
 }
 // Element mask of a partial tile: key validity, plus the scanline row rule
@@ -117,10 +121,11 @@ __device__ __forceinline__ bool admit(const AttnParams& p, const QInfo& qi, int 
   if (MODE != kModeScan) return true;
   if (!qi.valid) return false;
   if (p.tile_aligned || qi.text || j < p.text) return true;
-  return abs(qi.row - grid_row(p, j)) <= p.half_window;
+  // |row(j) - row| <= half_window for a valid image key j, without computing row(j)
+  return j >= qi.lo && j < qi.hi;
 }
 
-// One step of 64 keys: logical start, whether it needs element masking, and its route.
+// One step of 128 keys: logical start, whether it needs element masking, and its route.
 struct StepInfo {
   int k0;
   bool partial, int8;
