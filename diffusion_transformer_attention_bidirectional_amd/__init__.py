@@ -31,6 +31,7 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported dtype", -3: "unsuppo
 EXPORTS = ("attn_workspace_bytes", "attn_forward", "attn_forward_gated", "attn_block_workspace_bytes",
            "attn_block_forward", "attn_plan_info_get", "attn_route_map",
            "attn_block_mask", "attn_item_order", "attn_quantize", "attn_int8_scores", "attn_mask_row_counts",
+           "attn_device_plan", "attn_launch_items",
            "attn_mfma_probe", "attn_set_kernel_events", "attn_status_string", "attn_last_error")
 
 
@@ -104,7 +105,9 @@ def load_library(path: str = LIB_PATH):
         "attn_item_order": [P(AttnArgs), i32, vp, ctypes.c_int64],
         "attn_quantize": [P(AttnArgs), P(AttnTensor), P(AttnTensor), vp, sz, vp, vp, vp, vp, vp, vp],
         "attn_int8_scores": [P(AttnArgs), P(AttnTensor), P(AttnTensor), vp, sz, vp, i32, vp, vp],
-        "attn_mask_row_counts": [P(AttnArgs), vp, vp],
+        "attn_mask_row_counts": [P(AttnArgs), vp, sz, vp, vp],
+        "attn_device_plan": [P(AttnArgs), vp, sz, vp, vp, vp, vp, vp],
+        "attn_launch_items": [P(AttnArgs), i32, i32, vp, ctypes.c_int64, P(ctypes.c_int64)],
         "attn_mfma_probe": [i32, i32, i32, vp, P(ctypes.c_int64), vp],
         "attn_set_kernel_events": [vp, vp],
     }
@@ -332,6 +335,18 @@ def item_order(args: AttnArgs, slice_index: int = 0) -> np.ndarray:
     return out[:n]
 
 
+def launch_items(args: AttnArgs, slice_index: int, cus: int) -> np.ndarray:
+    """Work items of one attention launch (host only): int32 [workgroups, 4] of (global
+    64-query tile, pair, key-range part, parts) per workgroup, on a device with `cus` compute
+    units."""
+    lib = load_library()
+    n = ctypes.c_int64(0)
+    _check(lib.attn_launch_items(ctypes.byref(args), int(slice_index), int(cus), None, 0, ctypes.byref(n)))
+    out = np.zeros((max(n.value, 1), 4), dtype=np.int32)
+    _check(lib.attn_launch_items(ctypes.byref(args), int(slice_index), int(cus), out.ctypes.data, n.value, None))
+    return out[:n.value]
+
+
 # ---------------------------------------------------------------- device debug views
 def quantize(q, k, args: AttnArgs, stream=None) -> dict:
     """smooth_k mean, INT8 codes and scales of K and Q as the attention call computes them."""
@@ -368,10 +383,30 @@ def int8_scores(q, k, args: AttnArgs, tiles, stream=None):
 
 
 def mask_row_counts(args: AttnArgs, device="cuda", stream=None):
-    """Keys admitted per logical query row, as the attention kernel's mask evaluates them."""
+    """Keys admitted per logical query row, as the attention kernel's tile lists (built on the
+    device) and element mask evaluate them."""
     import torch
     n = plan_info(args)["logical_tokens"]
-    out = torch.empty(n, dtype=torch.int32, device=device)
-    _check(load_library().attn_mask_row_counts(ctypes.byref(args), out.data_ptr(),
-                                               _stream_handle(stream, torch.device(device))))
+    dev = torch.device(device)
+    out = torch.empty(n, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(workspace_bytes(args), 256), dtype=torch.uint8, device=dev)
+    _check(load_library().attn_mask_row_counts(ctypes.byref(args), ws.data_ptr(), ws.numel(), out.data_ptr(),
+                                               _stream_handle(stream, dev)))
     return out
+
+
+def device_plan(args: AttnArgs, device="cuda", stream=None) -> dict:
+    """The per-call plan as attn_forward builds it on the device (TileMix with INT8 tiles,
+    scanline): map [nb, nb] uint8, lists [nb, nb] int32, row_count and full_count [nb]."""
+    import torch
+    nb = plan_info(args)["n_blocks"]
+    dev = torch.device(device)
+    res = {"map": torch.empty((nb, nb), dtype=torch.uint8, device=dev),
+           "lists": torch.empty((nb, nb), dtype=torch.int32, device=dev),
+           "row_count": torch.empty(nb, dtype=torch.int32, device=dev),
+           "full_count": torch.empty(nb, dtype=torch.int32, device=dev)}
+    ws = torch.empty(max(workspace_bytes(args), 256), dtype=torch.uint8, device=dev)
+    _check(load_library().attn_device_plan(ctypes.byref(args), ws.data_ptr(), ws.numel(), res["map"].data_ptr(),
+                                           res["lists"].data_ptr(), res["row_count"].data_ptr(),
+                                           res["full_count"].data_ptr(), _stream_handle(stream, dev)))
+    return res

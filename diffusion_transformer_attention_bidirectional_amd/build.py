@@ -24,8 +24,13 @@ LIB = os.path.join(PKG, "libkrea_attn.so")
 BUILD = os.path.join(PKG, "_build")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC, "-Wall"]
-# -fno-honor-nans: no kernel produces or consumes a NaN (masked scores are -inf and the
-# running max starts finite), so max reductions need no NaN-quieting instructions.
+# The host units are plain C++ (hipcc would otherwise compile a .cpp file as HIP source
+# for a default GPU as well).
+HOST = ["-x", "c++", "-I", "/opt/rocm/include"]
+# -fno-honor-nans: from finite inputs no kernel produces or consumes a NaN: masked scores
+# are -inf and never meet another -inf (the running max starts finite), and the max-skip
+# rule keeps every probability finite in the P operand's type (at most 2^24 in bf16, 2^15
+# in fp16), so max reductions need no NaN-quieting instructions.
 DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]
 
@@ -49,9 +54,9 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
     units = [
-        ("plan.cpp", COMMON),
-        ("capi.cpp", COMMON + ["-D__HIP_PLATFORM_AMD__"]),
-        ("gemm.cpp", COMMON + ["-D__HIP_PLATFORM_AMD__"]),
+        ("plan.cpp", COMMON + HOST),
+        ("capi.cpp", COMMON + HOST + ["-D__HIP_PLATFORM_AMD__"]),
+        ("gemm.cpp", COMMON + HOST + ["-D__HIP_PLATFORM_AMD__"]),
         ("kernels.hip", COMMON + DEVICE),
     ]
     jobs = []

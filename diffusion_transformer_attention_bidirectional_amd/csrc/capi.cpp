@@ -28,81 +28,43 @@ attn_status fail(attn_status s, const std::string& msg) {
   return s;
 }
 
-// A plan plus its device copy.  Device layout: route map [nb * nb] (TileMix) or
-// row_ptr [nb + 1] int32, cols [nnz] int32, full_count [nb] int32 and the workgroup
-// order of every slice (scanline).
-struct DevicePlan {
+// A cached host plan: the layout, counts, the TileMix pick threshold and the scanline
+// geometry.  It holds no device memory: every call builds its tile lists on the device, in
+// its own workspace, from these scalars, so evicting a plan frees host memory only and never
+// touches memory that queued work or a captured graph may read.
+struct CachedPlan {
   std::string key;
-  int device = -1;
   krea::Plan plan;
-  unsigned char* dmem = nullptr;
-  size_t route_off = 0, row_ptr_off = 0, cols_off = 0, full_off = 0, order_off = 0;
-  ~DevicePlan() {
-    if (dmem) {
-      int cur = 0;
-      if (hipGetDevice(&cur) == hipSuccess && cur != device) (void)hipSetDevice(device);
-      (void)hipDeviceSynchronize();  // calls still in flight may read this plan
-      (void)hipFree(dmem);
-      if (cur != device) (void)hipSetDevice(cur);
-    }
-  }
 };
 
 constexpr size_t kMaxPlans = 8;  // the Scanline page keeps at most eight masks cached
 std::mutex g_mu;
-std::list<std::shared_ptr<DevicePlan>> g_cache;  // most recent first
+std::list<std::shared_ptr<const CachedPlan>> g_cache;  // most recent first
 
-attn_status get_plan(const attn_args& a, std::shared_ptr<DevicePlan>* out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return fail(ATTN_ERR_DEVICE, "hipGetDevice failed (no GPU?)");
+attn_status get_plan(const attn_args& a, std::shared_ptr<const CachedPlan>* out) {
   const std::string key = krea::plan_key(a);
-  std::lock_guard<std::mutex> lock(g_mu);
-  for (auto it = g_cache.begin(); it != g_cache.end(); ++it) {
-    if ((*it)->device == dev && (*it)->key == key) {
-      g_cache.splice(g_cache.begin(), g_cache, it);
-      *out = g_cache.front();
-      return ATTN_OK;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    for (auto it = g_cache.begin(); it != g_cache.end(); ++it) {
+      if ((*it)->key == key) {
+        g_cache.splice(g_cache.begin(), g_cache, it);
+        *out = g_cache.front();
+        return ATTN_OK;
+      }
     }
   }
-  auto dp = std::make_shared<DevicePlan>();
-  dp->key = key;
-  dp->device = dev;
-  dp->plan = krea::build_plan(a);
-  const krea::Plan& p = dp->plan;
-  size_t bytes = 0;
-  dp->route_off = bytes;
-  bytes += (p.route.size() + 255) & ~(size_t)255;
-  dp->row_ptr_off = bytes;
-  bytes += (p.row_ptr.size() * 4 + 255) & ~(size_t)255;
-  dp->cols_off = bytes;
-  bytes += (p.cols.size() * 4 + 255) & ~(size_t)255;
-  dp->full_off = bytes;
-  bytes += (p.full_count.size() * 4 + 255) & ~(size_t)255;
-  dp->order_off = bytes;
-  bytes += (p.item_order.size() * 4 + 255) & ~(size_t)255;
-  if (bytes == 0) bytes = 256;
-  if (hipMalloc((void**)&dp->dmem, bytes) != hipSuccess) {
-    dp->dmem = nullptr;
-    return fail(ATTN_ERR_DEVICE, "hipMalloc of the plan failed");
-  }
-  hipError_t e = hipSuccess;
-  if (!p.route.empty()) e = hipMemcpy(dp->dmem + dp->route_off, p.route.data(), p.route.size(), hipMemcpyHostToDevice);
-  if (e == hipSuccess && !p.row_ptr.empty())
-    e = hipMemcpy(dp->dmem + dp->row_ptr_off, p.row_ptr.data(), p.row_ptr.size() * 4, hipMemcpyHostToDevice);
-  if (e == hipSuccess && !p.cols.empty())
-    e = hipMemcpy(dp->dmem + dp->cols_off, p.cols.data(), p.cols.size() * 4, hipMemcpyHostToDevice);
-  if (e == hipSuccess && !p.full_count.empty())
-    e = hipMemcpy(dp->dmem + dp->full_off, p.full_count.data(), p.full_count.size() * 4, hipMemcpyHostToDevice);
-  if (e == hipSuccess && !p.item_order.empty())
-    e = hipMemcpy(dp->dmem + dp->order_off, p.item_order.data(), p.item_order.size() * 4, hipMemcpyHostToDevice);
-  if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, std::string("plan upload failed: ") + hipGetErrorString(e));
+  auto cp = std::make_shared<CachedPlan>();
+  cp->key = key;
+  cp->plan = krea::build_plan(a);
+  const krea::Plan& p = cp->plan;
   if (std::getenv("KREA_ATTN_LOG")) {
     std::fprintf(stderr, "[krea_attn] plan built: mode %d, %d blocks, %lld INT8 tiles, %lld active, %lld partial\n",
                  a.mode, p.lay.nb, (long long)p.int8_tiles, (long long)p.active_tiles, (long long)p.partial_tiles);
   }
-  g_cache.push_front(dp);
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_cache.push_front(cp);
   while (g_cache.size() > kMaxPlans) g_cache.pop_back();
-  *out = dp;
+  *out = cp;
   return ATTN_OK;
 }
 
@@ -130,10 +92,10 @@ float scale_of(const attn_args& a) {
   return a.softmax_scale > 0.0f ? a.softmax_scale : (float)(1.0 / std::sqrt((double)a.head_dim));
 }
 
-krea::AttnParams make_params(const attn_args& a, const DevicePlan* dp) {
+krea::AttnParams make_params(const attn_args& a, const krea::Plan& plan) {
   krea::AttnParams p;
   std::memset(&p, 0, sizeof(p));
-  const krea::Layout& l = dp->plan.lay;
+  const krea::Layout& l = plan.lay;
   p.batch = a.batch;
   p.heads_q = a.heads_q;
   p.heads_kv = a.heads_kv;
@@ -152,11 +114,33 @@ krea::AttnParams make_params(const attn_args& a, const DevicePlan* dp) {
   p.half_window = a.window / 2;
   p.tile_aligned = a.tile_aligned ? 1 : 0;
   p.smooth_k = a.smooth_k ? 1 : 0;
-  if (!dp->plan.route.empty()) p.route = dp->dmem + dp->route_off;
-  if (!dp->plan.row_ptr.empty()) p.row_ptr = (const int32_t*)(dp->dmem + dp->row_ptr_off);
-  if (!dp->plan.cols.empty()) p.cols_list = (const int32_t*)(dp->dmem + dp->cols_off);
-  if (!dp->plan.full_count.empty()) p.full_count = (const int32_t*)(dp->dmem + dp->full_off);
+  p.split = 1;
   return p;
+}
+
+// The device plan builder's rule and outputs, in workspace `ws` (TileMix with INT8 tiles and
+// scanline; null otherwise), and the plan pointers the attention kernel reads.
+bool plan_build(const attn_args& a, const krea::Plan& plan, const krea::WorkspaceLayout& w, unsigned char* ws,
+                krea::PlanBuild* pb, krea::AttnParams* p) {
+  const bool tilemix8 = a.mode == ATTN_TILEMIX && plan.int8_tiles > 0;
+  if (!(tilemix8 || a.mode == ATTN_SCANLINE) || !w.has_plan) return false;
+  std::memset(pb, 0, sizeof(*pb));
+  pb->mode = a.mode;
+  pb->nb = plan.lay.nb;
+  pb->n = plan.lay.n;
+  pb->route = plan.route_rule;
+  pb->geom = plan.geom;
+  pb->map = ws + w.plan_map;
+  pb->lists = (int32_t*)(ws + w.plan_lists);
+  pb->row_count = (int32_t*)(ws + w.plan_rows);
+  pb->full_count = (int32_t*)(ws + w.plan_full);
+  if (p != nullptr) {
+    if (tilemix8) p->route = pb->map;
+    p->cols_list = pb->lists;
+    p->row_count = pb->row_count;
+    p->full_count = pb->full_count;
+  }
+  return true;
 }
 
 krea::QuantParams make_quant(const attn_args& a, const attn_tensor* q, const attn_tensor* k, unsigned char* ws) {
@@ -199,42 +183,6 @@ int cu_count() {
   return cached[dev];
 }
 
-// Tail split of one launch of `items` work items with `nb` key steps each.  With one
-// workgroup per compute unit, the items run in waves of `cus`; the `rem` items of the
-// last, partial wave each run as `split` workgroups over consecutive key ranges.  Their
-// rem * split parts take ceil(rem * split / cus) waves of 1 / split of an item plus a
-// fixed cost per part (pipeline fill, publishing and merging the partial state: about
-// 0.15 of a whole item as measured on the Krea shapes, where a split of 2 beat 8), and
-// the split is chosen to minimise that (ties: the smaller split).
-void plan_tail(krea::AttnParams& p, int64_t items, int nb, int cus, int capacity) {
-  p.n_full = (int)items;
-  p.split = 1;
-  static const int max_split = [] {
-    const char* e = std::getenv("KREA_ATTN_TAIL_SPLIT");  // cap on the split (0 or 1: off)
-    return e ? std::atoi(e) : krea::kMaxTailSplit;
-  }();
-  if (cus <= 0 || capacity < 2 || nb < 2 || max_split < 2) return;
-  const int64_t rem = items % cus;
-  if (rem == 0 || rem > krea::kMaxTailItems) return;
-  int best = 1;
-  double best_cost = 1.0;  // unsplit: one more wave of whole items
-  constexpr double kPartCost = 0.15;
-  for (int s = 2; s <= std::min({max_split, krea::kMaxTailSplit, nb}); ++s) {
-    if (rem * s > capacity) break;
-    const double cost = (double)((rem * s + cus - 1) / cus) * (1.0 / s + kPartCost);
-    if (cost < best_cost - 1e-9) {
-      best_cost = cost;
-      best = s;
-    }
-  }
-  if (best < 2) return;
-  p.n_full = (int)(items - rem);
-  p.split = best;
-  if (std::getenv("KREA_ATTN_LOG"))
-    std::fprintf(stderr, "[krea_attn] launch: %lld items on %d CUs, %d whole, %lld split in %d\n", (long long)items,
-                 cus, p.n_full, (long long)rem, best);
-}
-
 attn_status hip_check(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
   return ATTN_OK;
@@ -257,16 +205,18 @@ attn_status attn_workspace_bytes(const attn_args* args, size_t* bytes) {
 
 namespace {
 
-// One attention call after validation and its pre-work (pre-pass, quantiser), ready to
-// launch its query slices: the block path changes q, gate and o between slices.
+// One attention call after validation and its pre-work (pre-pass with the plan build,
+// quantiser), ready to launch its query slices: the block path changes q, gate and o
+// between slices.
 struct Prepared {
   krea::AttnParams p;
-  std::shared_ptr<DevicePlan> dp;
+  std::shared_ptr<const CachedPlan> cp;
   krea::WorkspaceLayout w;
+  krea::TailRule tail;
   attn_args a;
   hipStream_t st = nullptr;
   bool bf16 = true;
-  int cus = 0, length = 0, chunk = 0;
+  int length = 0, chunk = 0;
   int slices() const { return (length + chunk - 1) / chunk; }
 };
 
@@ -287,24 +237,29 @@ attn_status prepare(const attn_args* args, const attn_tensor* q, const attn_tens
   if (!workspace || workspace_bytes < w.total)
     return fail(ATTN_ERR_WORKSPACE, "workspace smaller than attn_workspace_bytes()");
   if (workspace && ((uintptr_t)workspace & 255)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  std::shared_ptr<DevicePlan> dp;
-  if ((s = get_plan(a, &dp)) != ATTN_OK) return s;
+  std::shared_ptr<const CachedPlan> cp;
+  if ((s = get_plan(a, &cp)) != ATTN_OK) return s;
+  const krea::Plan& plan = cp->plan;
+  unsigned char* ws = (unsigned char*)workspace;
   hipStream_t st = (hipStream_t)stream;
-  krea::AttnParams p = make_params(a, dp.get());
+  krea::AttnParams p = make_params(a, plan);
   p.q = ref(q);
   p.k = ref(k);
   p.v = ref(v);
   set_output(p, o, gate);
   const bool bf16 = a.dtype == ATTN_BF16;
-  p.v_t = (const uint16_t*)((unsigned char*)workspace + w.v_t);
-  p.k_norm = (float*)((unsigned char*)workspace + w.k_norm);
+  p.v_t = (const uint16_t*)(ws + w.v_t);
+  p.k_norm = (float*)(ws + w.k_norm);
   if (a.mode != ATTN_SCANLINE) {
-    p.tail_count = (int32_t*)((unsigned char*)workspace + w.tail_count);
-    p.tail_state = (float*)((unsigned char*)workspace + w.tail_state);
+    p.tail_count = (int32_t*)(ws + w.tail_count);
+    p.tail_state = (float*)(ws + w.tail_state);
   }
-  if (a.mode == ATTN_TILEMIX && dp->plan.int8_tiles > 0) {
-    const krea::QuantParams qp = make_quant(a, q, k, (unsigned char*)workspace);
-    if ((s = hip_check(krea::launch_prepass(p, (uint16_t*)p.v_t, &qp, a.mode, bf16, st), "pre-pass launch")) != ATTN_OK)
+  krea::PlanBuild pb;
+  const bool has_plan = plan_build(a, plan, w, ws, &pb, &p);
+  if (a.mode == ATTN_TILEMIX && plan.int8_tiles > 0) {
+    const krea::QuantParams qp = make_quant(a, q, k, ws);
+    if ((s = hip_check(krea::launch_prepass(p, (uint16_t*)p.v_t, &qp, &pb, a.mode, bf16, st), "pre-pass launch")) !=
+        ATTN_OK)
       return s;
     if ((s = hip_check(krea::launch_quant_finish(qp, st), "quantiser launch")) != ATTN_OK) return s;
     p.k_mean = qp.k_mean;
@@ -314,19 +269,19 @@ attn_status prepare(const attn_args* args, const attn_tensor* q, const attn_tens
     p.q_inv = qp.q_inv;
     p.q_scale = qp.q_scale;
   } else {
-    if ((s = hip_check(krea::launch_prepass(p, (uint16_t*)p.v_t, nullptr, a.mode, bf16, st), "pre-pass launch")) !=
-        ATTN_OK)
+    if ((s = hip_check(krea::launch_prepass(p, (uint16_t*)p.v_t, nullptr, has_plan ? &pb : nullptr, a.mode, bf16,
+                                            st),
+                       "pre-pass launch")) != ATTN_OK)
       return s;
-    if (a.mode == ATTN_TILEMIX) p.route = nullptr;  // all FP16: the TileMix kernel never looks at INT8 state
   }
   out->p = p;
-  out->dp = dp;
+  out->cp = cp;
   out->w = w;
+  out->tail = krea::tail_rule(a, plan.lay, a.mode != ATTN_SCANLINE ? cu_count() : 0, w.tail_parts);
   out->a = a;
   out->st = st;
   out->bf16 = bf16;
-  out->cus = a.mode != ATTN_SCANLINE ? cu_count() : 0;
-  out->length = dp->plan.lay.length;
+  out->length = plan.lay.length;
   out->chunk = a.q_chunk > 0 ? a.q_chunk : out->length;
   return ATTN_OK;
 }
@@ -342,15 +297,22 @@ void set_output(krea::AttnParams& p, const attn_tensor* o, const attn_tensor* ga
   p.g_sh = gate ? gate->stride_h : 0;
 }
 
-attn_status launch_slice(Prepared& pr, int slice) {
+// The work items of one slice's launch: whole items and split ones, by the call's global
+// split rule, and the scanline order's text query tiles.
+void set_launch(Prepared& pr, int slice) {
   krea::AttnParams& p = pr.p;
   p.q_begin = slice * pr.chunk;
   p.q_end = std::min(pr.length, p.q_begin + pr.chunk);
-  plan_tail(p, krea::attention_items(pr.a, p.q_end - p.q_begin), pr.dp->plan.lay.nb, pr.cus, pr.w.tail_parts);
-  p.item_order = pr.dp->plan.item_order.empty()
-                     ? nullptr
-                     : (const int32_t*)(pr.dp->dmem + pr.dp->order_off) + pr.dp->plan.slice_begin[slice];
-  return hip_check(krea::launch_attention(p, pr.a.mode, pr.bf16, pr.st), "attention launch");
+  const int nq = (p.q_end - p.q_begin + 63) / 64;
+  const int64_t J = (int64_t)(pr.a.heads_q / 4) * pr.a.batch;
+  p.lsplit = krea::launch_split(pr.tail, J, p.q_begin / 64, nq);
+  p.split = p.lsplit.n_split > 0 ? pr.tail.split : 1;
+  p.n_long = pr.a.mode == ATTN_SCANLINE ? krea::scan_long_tiles(pr.cp->plan.lay, p.q_begin, nq) : 0;
+}
+
+attn_status launch_slice(Prepared& pr, int slice) {
+  set_launch(pr, slice);
+  return hip_check(krea::launch_attention(pr.p, pr.a.mode, pr.bf16, pr.st), "attention launch");
 }
 
 attn_status forward_impl(const attn_args* args, const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
@@ -562,12 +524,77 @@ attn_status attn_item_order(const attn_args* args, int32_t slice, int32_t* out, 
   attn_status s = check_args(args);
   if (s != ATTN_OK) return s;
   if (args->mode != ATTN_SCANLINE) return fail(ATTN_ERR_INVALID_ARG, "item order exists for ATTN_SCANLINE only");
-  const krea::Plan p = krea::build_plan(*args);
-  if (slice < 0 || slice >= (int32_t)p.slice_begin.size()) return fail(ATTN_ERR_INVALID_ARG, "slice out of range");
-  const size_t b = (size_t)p.slice_begin[slice];
-  const size_t e = slice + 1 < (int32_t)p.slice_begin.size() ? (size_t)p.slice_begin[slice + 1] : p.item_order.size();
-  if (!out || n != (int64_t)(e - b)) return fail(ATTN_ERR_INVALID_ARG, "out is NULL or n is not the launch's size");
-  std::memcpy(out, p.item_order.data() + b, (e - b) * sizeof(int32_t));
+  const krea::Layout l = krea::make_layout(*args);
+  const int chunk = args->q_chunk > 0 ? args->q_chunk : l.length;
+  const int slices = (l.length + chunk - 1) / chunk;
+  if (slice < 0 || slice >= slices) return fail(ATTN_ERR_INVALID_ARG, "slice out of range");
+  const int q0 = slice * chunk, q1 = std::min(l.length, q0 + chunk);
+  if (!out || n != krea::attention_items(*args, q1 - q0))
+    return fail(ATTN_ERR_INVALID_ARG, "out is NULL or n is not the launch's size");
+  const std::vector<int32_t> order = krea::scan_item_order(*args, l, q0, q1);
+  std::memcpy(out, order.data(), order.size() * sizeof(int32_t));
+  g_err.clear();
+  return ATTN_OK;
+}
+
+attn_status attn_launch_items(const attn_args* args, int32_t slice, int32_t cus, int32_t* out, int64_t n,
+                              int64_t* workgroups) {
+  attn_status s = check_args(args);
+  if (s != ATTN_OK) return s;
+  if (cus < 1) return fail(ATTN_ERR_INVALID_ARG, "cus must be >= 1");
+  const krea::Layout l = krea::make_layout(*args);
+  const int chunk = args->q_chunk > 0 ? args->q_chunk : l.length;
+  const int slices = (l.length + chunk - 1) / chunk;
+  if (slice < 0 || slice >= slices) return fail(ATTN_ERR_INVALID_ARG, "slice out of range");
+  const int q0 = slice * chunk, q1 = std::min(l.length, q0 + chunk), nq = (q1 - q0 + 63) / 64;
+  const krea::TailRule t = krea::tail_rule(*args, l, cus, krea::workspace_layout(*args).tail_parts);
+  const int64_t J = (int64_t)(args->heads_q / 4) * args->batch;
+  const krea::LaunchSplit ls = krea::launch_split(t, J, q0 / 64, nq);
+  const int split = ls.n_split > 0 ? t.split : 1;
+  const int64_t grid = ls.n_full + ls.n_split * split;
+  if (workgroups) *workgroups = grid;
+  if (!out) {
+    g_err.clear();
+    return ATTN_OK;
+  }
+  if (n != grid) return fail(ATTN_ERR_INVALID_ARG, "n is not the launch's workgroup count");
+  const bool scan = args->mode == ATTN_SCANLINE;
+  const int n_long = scan ? krea::scan_long_tiles(l, q0, nq) : 0;
+  for (int64_t L = 0; L < grid; ++L) {
+    const krea::LaunchItem li = krea::launch_item(scan, ls, split, n_long, L);
+    out[4 * L] = (int32_t)(q0 / 64 + li.qt);
+    out[4 * L + 1] = (int32_t)li.j;
+    out[4 * L + 2] = li.part;
+    out[4 * L + 3] = li.nparts;
+  }
+  g_err.clear();
+  return ATTN_OK;
+}
+
+attn_status attn_device_plan(const attn_args* args, void* workspace, size_t workspace_bytes, uint8_t* map,
+                             int32_t* lists, int32_t* row_count, int32_t* full_count, void* stream) {
+  attn_status s = check_args(args);
+  if (s != ATTN_OK) return s;
+  const krea::WorkspaceLayout w = krea::workspace_layout(*args);
+  if (!workspace || workspace_bytes < w.total) return fail(ATTN_ERR_WORKSPACE, "workspace too small");
+  if ((uintptr_t)workspace & 255) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  std::shared_ptr<const CachedPlan> cp;
+  if ((s = get_plan(*args, &cp)) != ATTN_OK) return s;
+  krea::PlanBuild pb;
+  if (!plan_build(*args, cp->plan, w, (unsigned char*)workspace, &pb, nullptr))
+    return fail(ATTN_ERR_INVALID_ARG, "a device plan exists for ATTN_SCANLINE and for ATTN_TILEMIX with INT8 tiles");
+  hipStream_t st = (hipStream_t)stream;
+  if ((s = hip_check(krea::launch_plan(pb, st), "plan launch")) != ATTN_OK) return s;
+  const size_t nb = (size_t)pb.nb;
+  if (map && (s = hip_check(hipMemcpyAsync(map, pb.map, nb * nb, hipMemcpyDeviceToDevice, st), "copy"))) return s;
+  if (lists && (s = hip_check(hipMemcpyAsync(lists, pb.lists, nb * nb * 4, hipMemcpyDeviceToDevice, st), "copy")))
+    return s;
+  if (row_count &&
+      (s = hip_check(hipMemcpyAsync(row_count, pb.row_count, nb * 4, hipMemcpyDeviceToDevice, st), "copy")))
+    return s;
+  if (full_count &&
+      (s = hip_check(hipMemcpyAsync(full_count, pb.full_count, nb * 4, hipMemcpyDeviceToDevice, st), "copy")))
+    return s;
   g_err.clear();
   return ATTN_OK;
 }
@@ -610,12 +637,12 @@ attn_status attn_int8_scores(const attn_args* args, const attn_tensor* q, const 
   if (n_tiles < 0 || (n_tiles > 0 && (!tiles || !out))) return fail(ATTN_ERR_INVALID_ARG, "bad tile list");
   const krea::WorkspaceLayout w = krea::workspace_layout(*args);
   if (!workspace || workspace_bytes < w.total) return fail(ATTN_ERR_WORKSPACE, "workspace too small");
-  std::shared_ptr<DevicePlan> dp;
-  if ((s = get_plan(*args, &dp)) != ATTN_OK) return s;
+  std::shared_ptr<const CachedPlan> cp;
+  if ((s = get_plan(*args, &cp)) != ATTN_OK) return s;
   hipStream_t st = (hipStream_t)stream;
   const krea::QuantParams qp = make_quant(*args, q, k, (unsigned char*)workspace);
   if ((s = hip_check(krea::launch_quant(qp, st), "quantiser launch")) != ATTN_OK) return s;
-  krea::AttnParams p = make_params(*args, dp.get());
+  krea::AttnParams p = make_params(*args, cp->plan);
   p.q = ref(q);
   p.k = ref(k);
   p.k_codes = qp.k_codes;
@@ -626,14 +653,23 @@ attn_status attn_int8_scores(const attn_args* args, const attn_tensor* q, const 
   return ATTN_OK;
 }
 
-attn_status attn_mask_row_counts(const attn_args* args, int32_t* out, void* stream) {
+attn_status attn_mask_row_counts(const attn_args* args, void* workspace, size_t workspace_bytes, int32_t* out,
+                                 void* stream) {
   attn_status s = check_args(args);
   if (s != ATTN_OK) return s;
   if (!out) return fail(ATTN_ERR_INVALID_ARG, "out is NULL");
-  std::shared_ptr<DevicePlan> dp;
-  if ((s = get_plan(*args, &dp)) != ATTN_OK) return s;
-  const krea::AttnParams p = make_params(*args, dp.get());
-  if ((s = hip_check(krea::launch_mask_counts(p, args->mode, out, (hipStream_t)stream), "launch"))) return s;
+  const krea::WorkspaceLayout w = krea::workspace_layout(*args);
+  if (!workspace || workspace_bytes < w.total) return fail(ATTN_ERR_WORKSPACE, "workspace too small");
+  if ((uintptr_t)workspace & 255) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  std::shared_ptr<const CachedPlan> cp;
+  if ((s = get_plan(*args, &cp)) != ATTN_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  krea::AttnParams p = make_params(*args, cp->plan);
+  krea::PlanBuild pb;
+  if (plan_build(*args, cp->plan, w, (unsigned char*)workspace, &pb, &p) &&
+      (s = hip_check(krea::launch_plan(pb, st), "plan launch")) != ATTN_OK)
+    return s;
+  if ((s = hip_check(krea::launch_mask_counts(p, args->mode, out, st), "launch"))) return s;
   g_err.clear();
   return ATTN_OK;
 }

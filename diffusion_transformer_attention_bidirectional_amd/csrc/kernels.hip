@@ -58,10 +58,12 @@ constexpr float TAU = 8.0f;     // rescale O only when the running max grows by 
 // (with alpha = exp2(m - mnew) = 0).
 constexpr float kMinRunningMax = -1.0e30f;
 // A step of full tiles skips the row max when no score in it can exceed the running max
-// by more than TAU_SKIP (log2 units): by Cauchy-Schwarz, scale * q . k <= scale |q| |k|,
-// and |k| is bounded per 128-key block by the relayout pass.  Then every probability is
-// at most 2^TAU_SKIP, far inside the range of the bf16 P and the fp32 sums.
-constexpr float TAU_SKIP = 24.0f;
+// by more than tau_skip (log2 units): by Cauchy-Schwarz, scale * q . k <= scale |q| |k|,
+// and |k| is bounded per 128-key block by the relayout pass.  Then every probability of the
+// step is at most 2^tau_skip, which the P operand of the P V product must hold: bf16 has
+// fp32's exponent range (2^24 is far inside it), fp16 stops at 65504 < 2^16, so fp16
+// probabilities are kept at or below 2^15.
+constexpr float tau_skip(bool bf16) { return bf16 ? 24.0f : 15.0f; }
 
 // Loads of values that stay fixed for a whole launch (plan arrays, the pre-pass and
 // quantiser outputs) at wave-uniform addresses, through the constant address space: they
@@ -151,8 +153,8 @@ __device__ __forceinline__ StepInfo step_info(const AttnParams& p, int qa, int e
 template <int MODE>
 __device__ __forceinline__ int step_count(const AttnParams& p, int qa, int* e0) {
   if (MODE == kModeScan) {
-    *e0 = ld_uniform(p.row_ptr, qa);
-    return ld_uniform(p.row_ptr, qa + 1) - *e0;
+    *e0 = qa * p.nb;
+    return ld_uniform(p.row_count, qa);
   }
   *e0 = (MODE == kModeTileMix && p.cols_list != nullptr) ? qa * p.nb : 0;
   return p.nb;
@@ -348,42 +350,26 @@ __device__ __forceinline__ void load_q_frags(const AttnParams& p, int b, int h, 
   for (int s = 0; s < 8; ++s) qf[s] = ok ? *(const uint4*)(src + 8 * qk_chunk(s, lh)) : make_uint4(0, 0, 0, 0);
 }
 
-// Workgroup -> work item (query tile, head group, batch) and key-range part.  The
-// hardware deals workgroups to the 8 XCDs round robin.  Items [0, n_full) run whole, and
-// the remap gives each XCD a contiguous range of them, so the workgroups sharing one KV
-// head (and its K/V in that XCD's L2) run on the same XCD.  The workgroups after them are
-// the `split` parts of each remaining item, in dispatch order.
+// Workgroup -> work item (query tile, head group, batch) and key-range part.  The hardware
+// deals workgroups to the 8 XCDs round robin; the remap gives each XCD a contiguous range
+// of the whole items, so the workgroups sharing one KV head (and its K/V in that XCD's L2)
+// run on the same XCD, and likewise a contiguous range of the split items' parts.  Whole
+// and split items follow the call's split rule (a function of each item's global position,
+// plan_rules.hpp); scanline never splits and runs each XCD's text query tiles first.
 struct WorkItem {
   int qt, hg, b;
-  int part, nparts, slot;  // slot: index of the item among the split ones
+  int part, nparts, slot;  // slot: index of the item among the launch's split ones
 };
-__device__ __forceinline__ WorkItem work_item(const AttnParams& p, int n_qtiles, int n_hg) {
+template <int MODE>
+__device__ __forceinline__ WorkItem work_item(const AttnParams& p, int n_hg) {
+  const LaunchItem li = launch_item(MODE == kModeScan, p.lsplit, p.split, p.n_long, blockIdx.x);
   WorkItem w;
-  const int L = blockIdx.x;
-  int item;
-  if (L < p.n_full) {
-    if (p.item_order != nullptr) {
-      item = ld_uniform(p.item_order, L);  // the same XCD ranges, longest items first
-    } else {
-      const int total = p.n_full;
-      const int xcd = L & 7, idx = L >> 3;
-      const int per = total >> 3, rem = total & 7;
-      item = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
-    }
-    w.part = 0;
-    w.nparts = 1;
-    w.slot = -1;
-  } else {
-    const int t = L - p.n_full;
-    w.slot = t / p.split;
-    w.part = t - w.slot * p.split;
-    w.nparts = p.split;
-    item = p.n_full + w.slot;
-  }
-  w.qt = item % n_qtiles;
-  const int rest = item / n_qtiles;
-  w.hg = rest % n_hg;
-  w.b = rest / n_hg;
+  w.qt = (int)li.qt;
+  w.hg = (int)(li.j % n_hg);
+  w.b = (int)(li.j / n_hg);
+  w.part = li.part;
+  w.nparts = li.nparts;
+  w.slot = li.slot;
   return w;
 }
 
@@ -651,9 +637,9 @@ __device__ __forceinline__ void full_step(const AttnParams& p, int i, int s0, in
   if (int8) {
     // |q8 . k8| <= |q8| |k8| (exact integers), so the score is at most this bound
     const int64_t tile = ((int64_t)b * p.heads_kv + g) * p.nb + (cur.k0 >> 7);
-    nomax = __all(qn8 * ld_uniform(p.k_norm8, tile) * ld_uniform(p.k_scale, tile) + qadd <= ws.m + TAU_SKIP);
+    nomax = __all(qn8 * ld_uniform(p.k_norm8, tile) * ld_uniform(p.k_scale, tile) + qadd <= ws.m + tau_skip(BF16));
   } else {
-    nomax = __all(qn * ld_uniform(knorm, cur.k0 >> 7) <= ws.m + TAU_SKIP);
+    nomax = __all(qn * ld_uniform(knorm, cur.k0 >> 7) <= ws.m + tau_skip(BF16));
   }
   attn_step<BF16, MODE, false, KIND, NEXTK>(p, sa, sb, cur, nxt, has_next, b, g, wave, lane, qf, q8f, qinfo, qadd,
                                             sq_l2, nomax, S0, S1, pp, ws);
@@ -666,7 +652,7 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, lh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const WorkItem wi = work_item(p, (p.q_end - p.q_begin + QT - 1) / QT, p.heads_q / 4);
+  const WorkItem wi = work_item<MODE>(p, p.heads_q / 4);
   const int qt = wi.qt, hg = wi.hg, b = wi.b;
   const int h = hg * 4 + (wave & 3);
   const int g = (hg * 4) / p.group;
@@ -933,6 +919,87 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
   }
 }
 
+// ---------------------------------------------------------------- device plan
+// The per-call plan, built in the workspace from the call's scalars by the rules of
+// plan_rules.hpp (the host planner evaluates the same ones): for query block a, the key
+// blocks the attention kernel visits, in the order it visits them, at lists[a * nb ..].
+//   TileMix ("Krea 2 TileMix Attention (FP16/INT8 tiles)", "What it actually patches"):
+//     the route of every tile into map; the FP16 full tiles, then the INT8 full tiles, each
+//     in key order, then the ragged last block; full_count[a] = the FP16 full tiles.
+//   Scanline ("Krea 2 Scanline Attention", "What the mask actually is"): the class of every
+//     tile (0 skip, 1 full, 2 partial) into map; the full tiles, then the partial ones
+//     (entry | 1 << 16), each in key order; row_count[a] entries, full_count[a] full.
+
+// Appends, in thread order, the values of the threads with `sel` to out[base ..] (256
+// threads, all calling); returns the new end.  sh: 4 ints of LDS.
+__device__ __forceinline__ int emit_ordered(bool sel, int value, int32_t* out, int base, int* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t m = __ballot(sel);
+  const int before = __popcll(m & ((1ull << lane) - 1ull));
+  if (lane == 0) sh[wave] = __popcll(m);
+  __syncthreads();
+  int off = base;
+  for (int w = 0; w < wave; ++w) off += sh[w];
+  const int total = sh[0] + sh[1] + sh[2] + sh[3];
+  __syncthreads();
+  if (sel) out[off + before] = value;
+  return base + total;
+}
+
+// Row a of the plan, by one workgroup of 256 threads.
+__device__ void build_plan_row(const PlanBuild& pb, int a, int* sh) {
+  const int nb = pb.nb, tid = threadIdx.x;
+  uint8_t* map = pb.map + (int64_t)a * nb;
+  int32_t* list = pb.lists + (int64_t)a * nb;
+  int end = 0, nfirst = 0;
+  if (pb.mode == kModeTileMix) {
+    const int nfull = (pb.n % KT) ? nb - 1 : nb;
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int b0 = 0; b0 < nfull; b0 += 256) {
+        const int b = b0 + tid;
+        bool sel = false;
+        if (b < nfull) {
+          const bool i8 = route_is_int8(pb.route, a, b);
+          if (pass == 0) map[b] = i8 ? 1 : 0;
+          sel = i8 == (pass == 1);
+        }
+        end = emit_ordered(sel, b, list, end, sh);
+      }
+      if (pass == 0) nfirst = end;
+    }
+    if (nfull < nb && tid == 0) {
+      map[nb - 1] = route_is_int8(pb.route, a, nb - 1) ? 1 : 0;
+      list[end] = nb - 1;
+    }
+    end = nb;
+  } else {
+    const TileSpan qs = tile_span(pb.geom, a);
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int b0 = 0; b0 < nb; b0 += 256) {
+        const int b = b0 + tid;
+        bool sel = false;
+        if (b < nb) {
+          const int cls = scan_tile_class(pb.geom, qs, tile_span(pb.geom, b));
+          if (pass == 0) map[b] = (uint8_t)cls;
+          sel = cls == pass + 1;
+        }
+        end = emit_ordered(sel, pass == 0 ? b : (b | (1 << 16)), list, end, sh);
+      }
+      if (pass == 0) nfirst = end;
+    }
+  }
+  if (tid == 0) {
+    pb.row_count[a] = end;
+    pb.full_count[a] = nfirst;
+  }
+}
+
+// The plan alone (debug views): one workgroup per query block.
+__global__ void __launch_bounds__(256) plan_kernel(const PlanBuild pb) {
+  __shared__ int sh[4];
+  build_plan_row(pb, blockIdx.x, sh);
+}
+
 // ---------------------------------------------------------------- per-block pre-pass
 // Everything the attention kernel needs from one 128-key block, in one pass over the
 // tensors.  One workgroup of 256 threads per (key block kb, KV head g, batch b):
@@ -941,13 +1008,15 @@ __global__ void __launch_bounds__(512) attn_fwd_kernel(const AttnParams p) {
 //     through LDS row-major and comes back through transpose reads as exactly the
 //     fragments the attention kernel reads;
 //   * the bound on |k| over the block's keys (when p.k_norm is given);
+//   * with pb (TileMix with INT8 tiles, scanline), row kb of the call's plan;
 //   * QUANT, the TileMix quantiser inputs ("Krea 2 TileMix Attention (FP16/INT8 tiles)",
 //     "The inputs that matter"): the fp64 column sums of K over the block's tokens, added in
 //     token order (smooth_k), and with QSCALE the INT8 scale of query tile kb of every query
 //     head that KV head g serves (a = max |q| over the tile, inv = fp32(127 / a),
 //     scale = fp32(a / 127)); the attention kernel derives the same scales itself.
 template <bool BF16, int MODE, bool QUANT, bool QSCALE>
-__global__ void __launch_bounds__(256) prepass_kernel(const AttnParams p, uint16_t* v_t, const QuantParams qp) {
+__global__ void __launch_bounds__(256) prepass_kernel(const AttnParams p, uint16_t* v_t, const QuantParams qp,
+                                                      const PlanBuild pb) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * SLAB];              // V tile, slab layout
   __shared__ __attribute__((aligned(1024))) unsigned char klds[QUANT ? KT * 256 : 16];  // K tile, row-major
   __shared__ float kmax[4];
@@ -1061,6 +1130,11 @@ __global__ void __launch_bounds__(256) prepass_kernel(const AttnParams p, uint16
         qp.q_scale[idx] = a > 0.f ? __fdiv_rn(a, 127.0f) : 0.f;
       }
     }
+  }
+  // the plan: row kb, by the workgroups of the first KV head of the first sample
+  if (pb.lists != nullptr && g == 0 && b == 0) {
+    __shared__ int sh[4];
+    build_plan_row(pb, kb, sh);
   }
 }
 
@@ -1179,7 +1253,7 @@ __global__ void __launch_bounds__(256) q_codes_kernel(const QuantParams p, int8_
 // ---------------------------------------------------------------- debug views
 // INT32 q8 . k8 of chosen 128x128 tiles through the attention kernel's INT8 path:
 // the same Q fragment load, in-register Q codes, INT8 K DMA staging and LDS layout,
-// and the same i8 MFMA fragment order.  One workgroup per tile; wave w owns query rows
+// and the same seeded i8 MFMA accumulation (qk_scores), read back as integers.  One workgroup per tile; wave w owns query rows
 // 32 w .. 32 w + 31 of the tile.
 template <bool BF16>
 __global__ void __launch_bounds__(256) int8_scores_kernel(const AttnParams p, const int32_t* tiles, int32_t* out) {
@@ -1205,15 +1279,13 @@ __global__ void __launch_bounds__(256) int8_scores_kernel(const AttnParams p, co
   int32_t* dst = out + (int64_t)blockIdx.x * 128 * 128;
 #pragma unroll
   for (int kb2 = 0; kb2 < KT / 32; ++kb2) {
-    i32x16 Si;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) Si[r] = 0;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) Si = mma8(*(const uint4*)(lds + k8_frag_off(kb2, s, lq, lh)), q8f[s], Si);
+    // the attention kernel's own INT8 product, accumulator seeded with kInt8BaseBits; the
+    // seed is taken off again in integer arithmetic
+    const f32x16 S = qk_scores<BF16, true>(lds, kb2, lq, lh, qf, q8f);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = 32 * kb2 + 8 * (r >> 2) + 4 * lh + (r & 3);
-      dst[(32 * wave + lq) * 128 + key] = Si[r];
+      dst[(32 * wave + lq) * 128 + key] = (int32_t)(__float_as_uint(S[r]) - kInt8BaseBits);
     }
   }
 }
@@ -1274,8 +1346,12 @@ hipError_t launch_quant(const QuantParams& p, hipStream_t s) {
   a.length = p.n;
   a.nb = p.nb;
   const dim3 gk(p.nb, p.heads_kv, p.batch);
-  if (p.bf16) hipLaunchKernelGGL((prepass_kernel<true, kModeTileMix, true, true>), gk, dim3(256), 0, s, a, nullptr, p);
-  else hipLaunchKernelGGL((prepass_kernel<false, kModeTileMix, true, true>), gk, dim3(256), 0, s, a, nullptr, p);
+  PlanBuild none;
+  memset(&none, 0, sizeof(none));
+  if (p.bf16)
+    hipLaunchKernelGGL((prepass_kernel<true, kModeTileMix, true, true>), gk, dim3(256), 0, s, a, nullptr, p, none);
+  else
+    hipLaunchKernelGGL((prepass_kernel<false, kModeTileMix, true, true>), gk, dim3(256), 0, s, a, nullptr, p, none);
   if (hipPeekAtLastError() != hipSuccess) return hipGetLastError();
   return launch_quant_finish(p, s);
 }
@@ -1291,9 +1367,8 @@ hipError_t launch_q_codes(const QuantParams& p, int8_t* q_codes, hipStream_t s) 
 
 template <bool BF16, int MODE>
 static void launch_attn_t(const AttnParams& p, hipStream_t s) {
-  const int items = (p.q_end - p.q_begin + QT - 1) / QT * (p.heads_q / 4) * p.batch;
-  const int grid = p.n_full + (items - p.n_full) * p.split;
-  hipLaunchKernelGGL((attn_fwd_kernel<BF16, MODE>), dim3(grid), dim3(64 * NWAVE), 0, s, p);
+  const int64_t grid = p.lsplit.n_full + p.lsplit.n_split * p.split;
+  hipLaunchKernelGGL((attn_fwd_kernel<BF16, MODE>), dim3((uint32_t)grid), dim3(64 * NWAVE), 0, s, p);
 }
 
 hipError_t launch_attention(const AttnParams& p, int mode, bool bf16, hipStream_t s) {
@@ -1309,21 +1384,35 @@ hipError_t launch_attention(const AttnParams& p, int mode, bool bf16, hipStream_
   return hipGetLastError();
 }
 
-hipError_t launch_prepass(const AttnParams& p, uint16_t* v_t, const QuantParams* qp, int mode, bool bf16,
-                          hipStream_t s) {
+hipError_t launch_prepass(const AttnParams& p, uint16_t* v_t, const QuantParams* qp, const PlanBuild* pb, int mode,
+                          bool bf16, hipStream_t s) {
   const dim3 grid(p.nb, p.heads_kv, p.batch);
-  QuantParams none;
-  memset(&none, 0, sizeof(none));
+  QuantParams noq;
+  memset(&noq, 0, sizeof(noq));
+  PlanBuild nop;
+  memset(&nop, 0, sizeof(nop));
+  const PlanBuild& b = pb != nullptr ? *pb : nop;
   if (qp != nullptr) {
-    if (bf16) hipLaunchKernelGGL((prepass_kernel<true, kModeTileMix, true, false>), grid, dim3(256), 0, s, p, v_t, *qp);
-    else hipLaunchKernelGGL((prepass_kernel<false, kModeTileMix, true, false>), grid, dim3(256), 0, s, p, v_t, *qp);
+    if (bf16)
+      hipLaunchKernelGGL((prepass_kernel<true, kModeTileMix, true, false>), grid, dim3(256), 0, s, p, v_t, *qp, b);
+    else
+      hipLaunchKernelGGL((prepass_kernel<false, kModeTileMix, true, false>), grid, dim3(256), 0, s, p, v_t, *qp, b);
   } else if (bf16) {
-    if (mode == kModeScan) hipLaunchKernelGGL((prepass_kernel<true, kModeScan, false, false>), grid, dim3(256), 0, s, p, v_t, none);
-    else hipLaunchKernelGGL((prepass_kernel<true, kModeDense, false, false>), grid, dim3(256), 0, s, p, v_t, none);
+    if (mode == kModeScan)
+      hipLaunchKernelGGL((prepass_kernel<true, kModeScan, false, false>), grid, dim3(256), 0, s, p, v_t, noq, b);
+    else
+      hipLaunchKernelGGL((prepass_kernel<true, kModeDense, false, false>), grid, dim3(256), 0, s, p, v_t, noq, b);
   } else {
-    if (mode == kModeScan) hipLaunchKernelGGL((prepass_kernel<false, kModeScan, false, false>), grid, dim3(256), 0, s, p, v_t, none);
-    else hipLaunchKernelGGL((prepass_kernel<false, kModeDense, false, false>), grid, dim3(256), 0, s, p, v_t, none);
+    if (mode == kModeScan)
+      hipLaunchKernelGGL((prepass_kernel<false, kModeScan, false, false>), grid, dim3(256), 0, s, p, v_t, noq, b);
+    else
+      hipLaunchKernelGGL((prepass_kernel<false, kModeDense, false, false>), grid, dim3(256), 0, s, p, v_t, noq, b);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_plan(const PlanBuild& pb, hipStream_t s) {
+  hipLaunchKernelGGL(plan_kernel, dim3(pb.nb), dim3(256), 0, s, pb);
   return hipGetLastError();
 }
 

@@ -5,6 +5,8 @@
 
 #include <cstdint>
 
+#include "plan_rules.hpp"
+
 namespace krea {
 
 struct TensorRef {
@@ -34,14 +36,15 @@ struct AttnParams {
   int half_window;     // window / 2 (scanline)
   int tile_aligned;
   int smooth_k;
-  const uint8_t* route;    // TileMix [nb * nb]
-  const int32_t* row_ptr;  // scanline tile lists
-  // per query block key lists: scanline [row_ptr[a], row_ptr[a + 1]) entries of
-  // (key block) | (partial << 16); TileMix with INT8 tiles nb key blocks at a * nb,
-  // FP16 full tiles, then INT8 full tiles, then the ragged block (null: key order)
+  // Per-call plan in the workspace, written by the plan builder of the pre-pass:
+  const uint8_t* route;       // TileMix [nb * nb], 1 = INT8 (null: every tile FP16)
+  // per query block a, the key-block list at a * nb: scanline entries (key block) |
+  // (partial << 16), full tiles first, row_count[a] entries; TileMix with INT8 tiles all nb
+  // key blocks, FP16 full tiles, then INT8 full tiles, then the ragged block (null: key
+  // order)
   const int32_t* cols_list;
+  const int32_t* row_count;   // scanline: entries of each list
   const int32_t* full_count;  // leading full tiles of each list (TileMix: FP16 full tiles)
-  const int32_t* item_order;  // scanline: work item of each workgroup of this launch
   const float* k_mean;     // [B, Hkv, 128]
   const int8_t* k_codes;   // [B, Hkv, nb, 128, 128]
   const float* k_scale;    // [B, Hkv, nb]
@@ -50,11 +53,30 @@ struct AttnParams {
   const float* q_scale;    // [B, Hq, nb]
   const uint16_t* v_t;     // V^T tiles [B, Hkv, nb, 128 channels, 128 keys] (keys in P^T order)
   float* k_norm;           // [B, Hkv, nb] upper bound of |k| over each 128-key block (relayout pass)
-  // Tail split of this launch: items [0, n_full) run whole; each later item runs as
-  // `split` workgroups over consecutive key ranges, merged through tail_count/tail_state.
-  int n_full, split;
+  // Work items of this launch (query tile, pair j = head group + head groups * batch) and
+  // the split tail (a rule of the item's global position): workgroups [0, lsplit.n_full) run
+  // whole items, the later ones the `split` parts of each split item, merged through
+  // tail_count / tail_state.  Scanline never splits, and orders its items text first.
+  LaunchSplit lsplit;
+  int split;
+  int n_long;              // scanline: query tiles of the launch that hold text queries
   int32_t* tail_count;     // [256] (one per split item), zero between launches
   float* tail_state;       // [parts][8 waves][66][64 lanes]
+};
+
+// Output pointers of the device plan builder (regions of the workspace) and the rule it
+// evaluates.  TileMix: route map, lists and FP16 full counts; scanline: block mask (0 skip,
+// 1 full, 2 partial), lists, entry and full counts.
+struct PlanBuild {
+  int mode;
+  int nb;
+  int n;                   // physical tokens (TileMix: a ragged last block when n % 128)
+  RouteRule route;
+  ScanGeom geom;
+  uint8_t* map;            // [nb * nb]
+  int32_t* lists;          // [nb * nb]
+  int32_t* row_count;      // [nb]
+  int32_t* full_count;     // [nb]
 };
 
 // Quantiser stage for TileMix (smooth_k mean, K codes, Q scales).
@@ -77,10 +99,12 @@ hipError_t launch_quant(const QuantParams& p, hipStream_t s);
 // Mean and K codes after a pre-pass that computed the K column sums and Q scales.
 hipError_t launch_quant_finish(const QuantParams& p, hipStream_t s);
 hipError_t launch_attention(const AttnParams& p, int mode, bool bf16, hipStream_t s);
-// Per-block pre-pass of attn_forward: V^T tiles, key-norm bounds, tail counters and, with
-// qp (TileMix), the K column sums and Q scales.
-hipError_t launch_prepass(const AttnParams& p, uint16_t* v_t, const QuantParams* qp, int mode, bool bf16,
-                          hipStream_t s);
+// The per-call pre-pass of attn_forward: V^T tiles, key-norm bounds, tail counters, with qp
+// (TileMix) the K column sums and Q scales, and with pb the plan rows (one per key block).
+hipError_t launch_prepass(const AttnParams& p, uint16_t* v_t, const QuantParams* qp, const PlanBuild* pb, int mode,
+                          bool bf16, hipStream_t s);
+// The plan builder alone (debug views).
+hipError_t launch_plan(const PlanBuild& pb, hipStream_t s);
 hipError_t launch_q_codes(const QuantParams& p, int8_t* q_codes, hipStream_t s);
 hipError_t launch_int8_scores(const AttnParams& p, const int32_t* tiles, int n_tiles, int32_t* out,
                               bool bf16, hipStream_t s);

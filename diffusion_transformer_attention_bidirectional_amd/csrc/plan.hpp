@@ -1,6 +1,7 @@
-// Host planner: argument validation, logical token layout, TileMix route map,
-// scanline block mask and per-query-block tile lists, workspace layout.
-// Pure C++ (no HIP), so every rule here is testable without a GPU.
+// Host planner: argument validation, logical token layout, TileMix route rule and map,
+// scanline block mask, launch order and split-tail rule, workspace layout.  Pure C++ (no
+// HIP), so every rule here is testable without a GPU; the per-call tile lists are built on
+// the device from the same rules (plan_rules.hpp).
 #pragma once
 
 #include <cstddef>
@@ -9,6 +10,7 @@
 #include <vector>
 
 #include "krea_attn.h"
+#include "plan_rules.hpp"
 
 namespace krea {
 
@@ -31,27 +33,12 @@ struct Layout {
 struct Plan {
   Layout lay;
   int mode = ATTN_DENSE;
-  std::vector<uint8_t> route;    // TileMix [nb * nb], 1 = INT8
-  std::vector<uint8_t> bmask;    // scanline [nb * nb], 0 skip / 1 full / 2 partial
-  // Per query block tile list.  Scanline: entries of block a are
-  // cols[row_ptr[a] .. row_ptr[a + 1]), each (key block) | (partial << 16); the
-  // full_count[a] full tiles come first, then the partial ones.  TileMix with INT8 tiles:
-  // all nb key blocks of block a at cols[a * nb ..], its full_count[a] FP16 full tiles
-  // first, then its INT8 full tiles, then the ragged last block (no row_ptr).  Online
-  // softmax does not depend on the order, and the kernel runs each kind in a loop of its
-  // own.
-  std::vector<int32_t> row_ptr;
-  std::vector<int32_t> cols;
-  std::vector<int32_t> full_count;
-  // Scanline: the order in which each launch (query slice) runs its work items,
-  // item_order[slice_begin[s] + L] being the item of workgroup L of slice s (see
-  // scan_item_order).
-  std::vector<int32_t> item_order;
-  std::vector<int32_t> slice_begin;
+  RouteRule route_rule;  // TileMix: the rule the device plan builder evaluates per tile
+  ScanGeom geom;         // scanline: the geometry of the block mask
   int64_t int8_tiles = 0, active_tiles = 0, partial_tiles = 0;
 };
 
-// Tail splitting (dense and TileMix): when the work items of a launch do not fill the
+// Tail splitting (dense and TileMix): when the work items of a whole call do not fill the
 // last wave of the machine, the key range of each item of that wave is split over several
 // workgroups whose partial softmax states are merged by the last one to finish.
 constexpr int kMaxTailParts = 256;   // at most this many partial states per launch
@@ -60,29 +47,36 @@ constexpr int kMaxTailSplit = 8;     // at most this many parts per item
 constexpr int kTailWaves = 8;        // waves per attention workgroup
 constexpr int kTailFloats = 66;      // per lane: 64 O^T values, running max, running sum
 constexpr size_t kTailPartBytes = (size_t)kTailWaves * kTailFloats * 64 * sizeof(float);
+// TileMix and scanline keep per-call tile lists of nb x nb entries in the workspace.
+constexpr int kMaxPlanBlocks = 4096;
 
 // Work items of one attention launch over `q_tokens` logical query positions:
 // 64-token query tiles x groups of 4 query heads x batch.
 int64_t attention_items(const attn_args& a, int q_tokens);
 
-// Workgroup -> work item order of a scanline launch over logical query rows
-// [q_begin, q_end).  Item t is (query tile t % nq, head group (t / nq) % G4, batch); the
-// hardware hands workgroup L to XCD L % 8, and workgroup L = x + 8 i runs the i-th item
-// of XCD x's contiguous range of items (so the items of one KV head share an L2, as in
-// the dense order).  Within each range the items run longest first (by key tiles, stable
-// for equal lengths): query tiles of text rows visit every key tile, image rows only
-// their band, and an order that starts the long items late leaves a tail.
-std::vector<int32_t> scan_item_order(const attn_args& a, const Plan& p, int q_begin, int q_end);
+// Scanline launch order over logical query rows [q_begin, q_end) (one launch): out[L] is the
+// item workgroup L runs (item t = query tile t % nq of head group (t / nq) % (Hq / 4), batch
+// t / (nq Hq / 4)); each XCD runs a contiguous range of items, text query tiles first.
+std::vector<int32_t> scan_item_order(const attn_args& a, const Layout& l, int q_begin, int q_end);
+// Query tiles of a scanline launch from q_begin that hold a text query.
+int scan_long_tiles(const Layout& l, int q_begin, int nq);
+
+// Split-tail rule of a whole call (a function of global positions only) on a device with
+// `cus` compute units and room for `capacity` partial states.
+TailRule tail_rule(const attn_args& a, const Layout& l, int cus, int capacity);
 
 // Offsets of the workspace regions (bytes, 256-aligned).  Every mode holds V^T tiles
-// [B, Hkv, nb, 128 channels, 128 keys] and the key-norm bounds; dense and TileMix add the tail-split counters
-// (int32 [kMaxTailItems]) and partial states (tail_parts x kTailPartBytes); TileMix adds
-// the quantiser state.
+// [B, Hkv, nb, 128 channels, 128 keys] and the key-norm bounds; dense and TileMix add the
+// tail-split counters (int32 [kMaxTailItems]) and partial states (tail_parts x
+// kTailPartBytes); TileMix and scanline add the per-call plan (map [nb * nb] u8, lists
+// [nb * nb] int32, row and full counts [nb] int32); TileMix adds the quantiser state.
 struct WorkspaceLayout {
   size_t v_t = 0;
   size_t k_norm = 0;  // fp32 [B, Hkv, nb]: largest key norm of each 128-key block
   size_t tail_count = 0, tail_state = 0;
   int tail_parts = 0;  // capacity of the partial-state region (0: never split)
+  size_t plan_map = 0, plan_lists = 0, plan_rows = 0, plan_full = 0;
+  bool has_plan = false;
   size_t k_part = 0, k_mean = 0, k_codes = 0, k_scale = 0, k_norm8 = 0, q_inv = 0, q_scale = 0;
   size_t total = 0;
 };
@@ -92,7 +86,8 @@ attn_status validate_args(const attn_args& a, std::string& err);
 Layout make_layout(const attn_args& a);
 WorkspaceLayout workspace_layout(const attn_args& a);
 
-uint64_t splitmix64(uint64_t x);
+RouteRule route_rule(const attn_args& a, const Layout& lay, int64_t* n_int8);
+ScanGeom scan_geom(const attn_args& a, const Layout& lay);
 std::vector<uint8_t> build_route_map(const attn_args& a, const Layout& lay, int64_t* n_int8);
 std::vector<uint8_t> build_block_mask(const attn_args& a, const Layout& lay);
 Plan build_plan(const attn_args& a);

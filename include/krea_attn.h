@@ -32,10 +32,17 @@
  *     aligned and strides multiples of 8 elements.
  *   - The caller owns q, k, v, o, the workspace and the stream.  Device entry points
  *     only enqueue work on the given HIP stream (NULL = the null stream) and return
- *     without synchronising.  The library owns a cache of at most 8 plans (route
- *     maps, block masks, tile lists) with their device copies, keyed by device and
- *     every shape and mode argument; a cache miss builds the plan on the host and
- *     copies it to the device synchronously before enqueueing.
+ *     without synchronising.  attn_forward and attn_forward_gated allocate no device or
+ *     pinned memory, copy nothing from the host and never wait for the device: they
+ *     enqueue kernel launches only, so a call can be captured into a HIP graph, also its
+ *     first call of a shape.
+ *   - Plans: the library keeps a host-only cache of at most 8 plans ("Krea 2 Scanline
+ *     Attention", "Where people get burned": masks cached by prompt length and
+ *     resolution), keyed by every shape and mode argument: the logical layout, counts,
+ *     the TileMix pick threshold and the scanline geometry (plain host memory).  Every
+ *     call builds its tile lists on the device, into its own workspace, from those
+ *     scalars; evicting a plan therefore frees host memory only, never memory that
+ *     queued work or a captured graph reads.
  *   - Every argument is validated before any device work.  Errors are returned as
  *     attn_status codes, never thrown; attn_last_error() gives a message for the
  *     calling thread.  There is no fallback path: an unsupported input is an error.
@@ -113,9 +120,10 @@ typedef struct {
 } attn_plan_info;
 
 /* Bytes of device workspace attn_forward needs for these arguments.  Every mode holds a
- * relayout of V (V^T tiles of 128 keys, the size of V rounded up to whole tiles); TileMix
- * adds the smooth_k partial sums and mean, INT8 K codes and scales, and Q scales.
- * Host only. */
+ * relayout of V (V^T tiles of 128 keys, the size of V rounded up to whole tiles); dense and
+ * TileMix add the split tail's counters and partial states; TileMix and scanline add the
+ * per-call plan (5 nb^2 + 8 nb bytes: map and tile lists); TileMix adds the smooth_k
+ * partial sums and mean, INT8 K codes and scales, and Q scales.  Host only. */
 attn_status attn_workspace_bytes(const attn_args* args, size_t* bytes);
 
 /* The attention call.  q, k, v are read, o is written (rows of every valid token;
@@ -192,6 +200,19 @@ attn_status attn_block_mask(const attn_args* args, uint8_t* out, int32_t nb);
  * Errors: not ATTN_SCANLINE, slice out of range, n not the launch's size, out NULL. */
 attn_status attn_item_order(const attn_args* args, int32_t slice, int32_t* out, int64_t n);
 
+/* Work items of one attention launch, as the kernel maps its workgroups to them, on a
+ * device with `cus` compute units (host only).  slice: the query slice (as attn_item_order);
+ * *workgroups (if not NULL) receives the launch's workgroup count (whole items plus the
+ * parts of split items); out (NULL: only the count) int32 [n][4], for workgroup L = (global
+ * 64-query tile, pair = head group + (Hq / 4) * batch, key-range part, parts of the item),
+ * n the workgroup count.  Dense and TileMix split the items of the last,
+ * partial wave of the whole call (Hq / 4 * batch * ceil(N / 64) items on `cus` units) into
+ * key-range parts; which items split depends only on the item's global position (its query
+ * tile and pair), so every query slicing computes each row the same way.  Errors: slice out
+ * of range, cus < 1, out given and n not the launch's workgroup count. */
+attn_status attn_launch_items(const attn_args* args, int32_t slice, int32_t cus, int32_t* out, int64_t n,
+                              int64_t* workgroups);
+
 /* Device debug exports.  They run the same device functions as attn_forward.
  *
  * attn_quantize: the smooth_k mean and per-tile INT8 stage of TileMix ("The inputs that
@@ -212,8 +233,25 @@ attn_status attn_int8_scores(const attn_args* args, const attn_tensor* q, const 
                              int32_t n_tiles, int32_t* out, void* stream);
 
 /* attn_mask_row_counts: number of keys each logical query row admits, evaluated by the
- * kernel's own tile list and element mask.  out: device int32 [logical_tokens]. */
-attn_status attn_mask_row_counts(const attn_args* args, int32_t* out, void* stream);
+ * kernel's own tile lists (built on the device into `workspace`, as attn_forward builds
+ * them) and element mask.  workspace: at least attn_workspace_bytes(), 256-byte aligned.
+ * out: device int32 [logical_tokens]. */
+attn_status attn_mask_row_counts(const attn_args* args, void* workspace, size_t workspace_bytes, int32_t* out,
+                                 void* stream);
+
+/* attn_device_plan: the per-call plan as attn_forward builds it on the device, copied out.
+ * For ATTN_TILEMIX with INT8 tiles and for ATTN_SCANLINE (anything else is
+ * ATTN_ERR_INVALID_ARG).  Each output is a device pointer or NULL:
+ *   map        uint8 [nb][nb]: TileMix route (1 INT8), scanline class (0 skip, 1 full,
+ *              2 partial) -- the same values as attn_route_map / attn_block_mask;
+ *   lists      int32 [nb][nb]: row a holds the key blocks query block a visits, in order
+ *              (TileMix: FP16 full tiles, INT8 full tiles, then the ragged last block, nb
+ *              entries; scanline: full tiles then partial ones as block | 1 << 16);
+ *   row_count  int32 [nb]: entries of each row (nb for TileMix);
+ *   full_count int32 [nb]: leading full tiles of each row (TileMix: FP16 full tiles).
+ * workspace: at least attn_workspace_bytes(), 256-byte aligned.  Async on stream. */
+attn_status attn_device_plan(const attn_args* args, void* workspace, size_t workspace_bytes, uint8_t* map,
+                             int32_t* lists, int32_t* row_count, int32_t* full_count, void* stream);
 
 /* Measurement hook.  With two hipEvent_t handles (created by the caller, who keeps
  * ownership), every later attn_forward on the calling thread records start_event on its

@@ -1,9 +1,11 @@
-"""HIP graph capture of the library's calls: after one eager call (which builds and uploads
-the plan, and for the block path picks the GEMM algorithms), a call captured into a graph
-must give the eager result on every replay, with the program's own eager work and
-synchronisations between the replays.  The attention path launches kernels only (no
-memset, copy or synchronisation once the plan is cached); the split tail's counters are
-reset by the pre-pass of each call, so replays start from the same state."""
+"""HIP graph capture of the library's calls: a call captured into a graph must give the eager
+result on every replay, with the program's own eager work and synchronisations between the
+replays.  The attention path launches kernels only -- no allocation, memset, host copy or
+synchronisation, not even on the first call of a shape: each call's pre-pass builds the tile
+lists in the call's workspace and resets the split tail's counters, so replays start from
+the same state, and the host plan cache holds no device memory a replay could read after an
+eviction.  The block path picks its GEMM algorithms on its first call of a shape, which
+waits for the stream, so it is captured after one eager call."""
 import numpy as np
 import pytest
 import torch
@@ -81,3 +83,46 @@ def test_block_graph_replays_match_eager(dev):
         assert np.all(np.abs(got - eager) <= bound), f"block replay {rep}"
         ka.block_forward(x, wq, wk, wv, wg, wo, y.clone(), workspace=ws, **kw)
         torch.cuda.synchronize()
+
+
+def _other_shapes(n):
+    """n small calls of distinct shapes (each its own plan) in every mode."""
+    from synth import Workload
+    out = []
+    for i in range(n):
+        mode = ("dense", "tilemix", "scanline")[i % 3]
+        extra = dict(pattern="band", percentage=0.5, band_blocks=1, smooth_k=True) if mode == "tilemix" else {}
+        out.append(Workload(name=f"o{i}", batch=1, heads_q=4, heads_kv=1, head_dim=128, text_tokens=30 + 7 * i,
+                            img_rows=5 + i, img_cols=17 + 2 * i, dtype="bf16", seed=300 + i, offset_std=0.5,
+                            mode=mode, window=3, **extra))
+    return out
+
+
+@pytest.mark.parametrize("name", ["1mp_band", "1mp_scanline"])
+def test_graph_captured_on_first_call_survives_plan_eviction(dev, name):
+    """A shape captured into a graph on its very first call, then more than the cache's 8
+    other plans built (the captured shape's plan is evicted and rebuilt) between replays:
+    every replay equals the eager result."""
+    w = WORKLOADS[name].with_(text_tokens=500)  # a shape no other test uses
+    w = w.with_(img_rows=63, img_cols=64)
+    q, k, v = (t.to(dev) for t in make_qkv(w))
+    kw = _kw(w)
+    ws = torch.empty(max(ka.workspace_bytes(ka.args_for(q, k, **kw)), 256), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ka.attention(q, k, v, out=out, workspace=ws, **kw)  # the shape's first call
+    others = [(o, tuple(t.to(dev) for t in make_qkv(o))) for o in _other_shapes(10)]
+    eager = None
+    for rep in range(3):
+        for o, (qo, ko, vo) in others:  # evicts the captured shape's plan
+            ka.attention(qo, ko, vo, **_kw(o))
+        torch.cuda.synchronize()
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        if eager is None:
+            eager = ka.attention(q, k, v, **kw)
+            torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"{name} replay {rep}"

@@ -128,8 +128,9 @@ ORDER_CASES = [
 @pytest.mark.parametrize("t,rows,cols,window,aligned,chunk,batch,hq", ORDER_CASES)
 def test_scanline_item_order(lib, t, rows, cols, window, aligned, chunk, batch, hq):
     """Each launch runs a permutation of its items; XCD x (workgroups L = x + 8 i) runs its
-    contiguous range of items, longest first by the key tiles of the item's query block
-    (zero for a tile of padding only), ties in item order."""
+    contiguous range of items, the query tiles holding text queries first (they visit every
+    key tile, the others only their band), each kind in item order.  The text tiles are the
+    longest items: checked against the block mask."""
     args = ka.make_args(batch=batch, heads_q=hq, heads_kv=hq // 4, text_tokens=t, img_rows=rows, img_cols=cols,
                         mode="scanline", window=window, tile_aligned=aligned, q_chunk=chunk)
     mask = plan_ref.block_mask(t, rows, cols, window, bool(aligned))
@@ -143,19 +144,25 @@ def test_scanline_item_order(lib, t, rows, cols, window, aligned, chunk, batch, 
         order = ka.item_order(args, si)
         assert order.shape == (n,) and sorted(order.tolist()) == list(range(n))
 
+        def is_text(item):
+            return q0 + 64 * (item % nq) < t
+
         def cost(item):
             lo = q0 + 64 * (item % nq)
             hi = min(lo + 64, q1)
             valid = lo < min(hi, t) or max(lo, lay.t_pad) < min(hi, lay.t_pad + rows * cols)
             return int((mask[lo // 128] != 0).sum()) if valid else 0
 
+        costs = [cost(i) for i in range(n)]
+        if any(is_text(i) for i in range(n)):
+            assert min(costs[i] for i in range(n) if is_text(i)) == max(costs)
         per, rem = divmod(n, 8)
         for x in range(8):
             base = x * (per + 1) if x < rem else rem * (per + 1) + (x - rem) * per
             cnt = per + 1 if x < rem else per
             got = order[x::8].tolist()
             assert len(got) == cnt and sorted(got) == list(range(base, base + cnt))
-            keys = [(-cost(i), i) for i in got]
+            keys = [(0 if is_text(i) else 1, i) for i in got]
             assert keys == sorted(keys)
     with pytest.raises(ka.KreaAttnError):
         ka.item_order(args, len(range(0, length, step)))
@@ -184,12 +191,15 @@ def test_workspace_sizes(lib):
     # 2 blocks, 4 items (4 query tiles of 64 x 1 head group): room for items x min(nb, 8) parts
     two = ka.make_args(text_tokens=200, img_rows=0, img_cols=0, heads_q=4, heads_kv=1)
     assert ka.workspace_bytes(two) == 2 * 128 * 128 * 2 + 256 + 1024 + 4 * 2 * TAIL_PART_BYTES
+    # scanline: padded logical length 256 (nb = 2), never split; the per-call plan: map
+    # [nb, nb] uint8, lists [nb, nb] int32, row and full counts [nb] int32
     scan = ka.make_args(text_tokens=77, img_rows=10, img_cols=12, heads_q=4, heads_kv=1, mode="scanline")
-    assert ka.workspace_bytes(scan) == 2 * 128 * 128 * 2 + 256  # padded logical length 256, never split
+    assert ka.workspace_bytes(scan) == 2 * 128 * 128 * 2 + 256 + 4 * 256
     tm = ka.make_args(text_tokens=512, img_rows=64, img_cols=64, mode="tilemix")
     n = ka.workspace_bytes(tm)
-    # plus at least the INT8 K codes: 12 KV heads x 36 blocks x 128 x 128
-    assert n >= dense + 12 * 36 * 128 * 128
+    # plus the plan (36 blocks) and at least the INT8 K codes: 12 KV heads x 36 blocks x 128 x 128
+    plan = _a256(36 * 36) + _a256(36 * 36 * 4) + 2 * _a256(36 * 4)
+    assert n >= dense + plan + 12 * 36 * 128 * 128
 
 
 def test_block_workspace_and_validation(lib):
@@ -325,3 +335,61 @@ def test_caller_policy_helpers(lib):
     assert ka.describe(scan) == ("krea_attn scanline: 48 q / 12 kv heads, 4608 tokens, 36x36 tiles, window 11 "
                                  "tile-aligned: 484 active (37.3 %), queries in slices of 1024")
     assert ka.describe(ka.make_args(text_tokens=5)).startswith("krea_attn dense: 48 q / 12 kv heads, 5 tokens")
+
+
+LAUNCH_CASES = [
+    # text, rows, cols, batch, heads_q, mode, chunks
+    (512, 64, 64, 1, 48, "dense", (0, 4096, 2048, 1024, 128)),    # 1 MP: 864 items, 96 in the last wave
+    (512, 128, 128, 1, 48, "tilemix", (0, 4096, 2048)),           # 4 MP: 3168 items
+    (77, 9, 13, 2, 8, "dense", (0, 128, 256)),                     # ragged, batch 2
+    (40, 10, 26, 1, 8, "tilemix", (0, 128)),
+    (512, 64, 64, 1, 48, "scanline", (0, 4096)),
+]
+
+
+def _launch_workgroups(args, lay_len, chunk, cus):
+    step = chunk if chunk > 0 else lay_len
+    jn = (args.heads_q // 4) * args.batch
+    items = {}
+    for si, q0 in enumerate(range(0, lay_len, step)):
+        nq = (min(lay_len, q0 + step) - q0 + 63) // 64
+        for qt, j, part, parts in ka.launch_items(args, si, cus).tolist():
+            assert q0 // 64 <= qt < q0 // 64 + nq and 0 <= j < jn
+            items.setdefault((qt, j), []).append((part, parts))
+    return items
+
+
+@pytest.mark.parametrize("t,rows,cols,batch,hq,mode,chunks", LAUNCH_CASES)
+@pytest.mark.parametrize("cus", [256, 80, 304])
+def test_split_rule_independent_of_slicing(lib, t, rows, cols, batch, hq, mode, chunks, cus):
+    """Every launch runs each of its (query tile, pair) items once, whole or as parts 0..s-1,
+    and which items split (and into how many parts) is the same under every query slicing:
+    so each query row is computed the same way whatever q_chunk is.  In the whole call the
+    split items are exactly the last wave's (G mod cus) items of highest rank."""
+    base = None
+    for chunk in chunks:
+        args = ka.make_args(batch=batch, heads_q=hq, heads_kv=hq // 4, text_tokens=t, img_rows=rows, img_cols=cols,
+                            mode=mode, q_chunk=chunk)
+        length = ka.plan_info(args)["logical_tokens"]
+        items = _launch_workgroups(args, length, chunk, cus)
+        nq_all = (length + 63) // 64
+        jn = (hq // 4) * batch
+        assert sorted(items) == [(q, j) for q in range(nq_all) for j in range(jn)]
+        split_of = {}
+        for key, parts in items.items():
+            s = parts[0][1]
+            assert sorted(parts) == [(p, s) for p in range(s)], (key, parts)
+            split_of[key] = s
+        if base is None:
+            base = split_of
+            G = nq_all * jn
+            rem = G % cus
+            split = {k: v for k, v in split_of.items() if v > 1}
+            if split:
+                assert mode != "scanline"
+                ranks = sorted(q * jn + j for q, j in split)
+                assert ranks == list(range(G - rem, G))
+        else:
+            assert split_of == base, f"q_chunk {chunk} splits differently"
+    if mode != "scanline" and (t, rows, cols) == (512, 64, 64) and cus == 256:
+        assert max(base.values()) == 2 and sum(v > 1 for v in base.values()) == 96
