@@ -28,7 +28,7 @@ PATTERNS = {"zero": 0, "one": 1, "band": 2, "all": 3}
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported dtype", -3: "unsupported shape",
           -4: "workspace too small", -5: "device error"}
 
-EXPORTS = ("attn_workspace_bytes", "attn_forward", "attn_forward_gated", "attn_block_workspace_bytes",
+EXPORTS = ("attn_workspace_bytes", "attn_forward", "attn_forward_gated", "attn_forward_noalloc", "attn_block_workspace_bytes",
            "attn_block_forward", "attn_plan_info_get", "attn_route_map",
            "attn_block_mask", "attn_item_order", "attn_quantize", "attn_int8_scores", "attn_mask_row_counts",
            "attn_device_plan", "attn_launch_items",
@@ -97,6 +97,7 @@ def load_library(path: str = LIB_PATH):
         "attn_forward": [P(AttnArgs), P(AttnTensor), P(AttnTensor), P(AttnTensor), P(AttnTensor), vp, sz, vp],
         "attn_forward_gated": [P(AttnArgs), P(AttnTensor), P(AttnTensor), P(AttnTensor), P(AttnTensor),
                                P(AttnTensor), vp, sz, vp],
+        "attn_forward_noalloc": [P(AttnArgs), P(AttnTensor), P(AttnTensor), P(AttnTensor), P(AttnTensor), vp],
         "attn_block_workspace_bytes": [P(AttnArgs), i32, P(sz)],
         "attn_block_forward": [P(AttnArgs), P(AttnBlockWeights), vp, vp, vp, sz, vp],
         "attn_plan_info_get": [P(AttnArgs), P(AttnPlanInfo)],
@@ -202,6 +203,17 @@ def attention(q, k, v, *, text_tokens, img_rows=0, img_cols=0, mode="dense", out
             raise KreaAttnError("gate must have q's shape and dtype")
         _check(lib.attn_forward_gated(ctypes.byref(args), tq, tk, tv, ctypes.byref(_tensor(gate)), to, wptr, wlen,
                                       st))
+    return out
+
+
+def attention_noalloc(q, k, v, out, *, text_tokens, img_rows=0, img_cols=0, mode="dense", stream=None, **kw):
+    """attention() through attn_forward_noalloc: the library's static device scratch serves as
+    the workspace, so nothing is allocated (the caller passes ``out``).  Calls that overlap
+    on one GPU share that scratch and race."""
+    args = args_for(q, k, text_tokens=text_tokens, img_rows=img_rows, img_cols=img_cols, mode=mode, **kw)
+    lib = load_library()
+    _check(lib.attn_forward_noalloc(ctypes.byref(args), *(ctypes.byref(_tensor(t)) for t in (q, k, v, out)),
+                                    _stream_handle(stream, q.device)))
     return out
 
 

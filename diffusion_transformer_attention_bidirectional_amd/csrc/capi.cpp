@@ -377,6 +377,22 @@ attn_status attn_forward(const attn_args* args, const attn_tensor* q, const attn
   return forward_impl(args, q, k, v, nullptr, o, workspace, workspace_bytes, stream);
 }
 
+attn_status attn_forward_noalloc(const attn_args* args, const attn_tensor* q, const attn_tensor* k,
+                                 const attn_tensor* v, const attn_tensor* o, void* stream) {
+  attn_status s = check_args(args);
+  if (s != ATTN_OK) return s;
+  const size_t need = krea::workspace_layout(*args).total;
+  if (need > krea::kScratchBytes) {
+    char msg[160];
+    std::snprintf(msg, sizeof(msg), "this call needs %zu bytes of workspace; the library's static scratch holds %zu",
+                  need, krea::kScratchBytes);
+    return fail(ATTN_ERR_WORKSPACE, msg);
+  }
+  void* ws = nullptr;
+  if ((s = hip_check(krea::scratch_region(&ws), "static scratch address")) != ATTN_OK) return s;
+  return forward_impl(args, q, k, v, nullptr, o, ws, krea::kScratchBytes, stream);
+}
+
 attn_status attn_block_workspace_bytes(const attn_args* args, int32_t model_dim, size_t* bytes) {
   attn_status s = check_args(args);
   if (s != ATTN_OK) return s;

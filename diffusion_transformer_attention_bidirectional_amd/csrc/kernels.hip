@@ -29,6 +29,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "kernels.hpp"
 
@@ -1414,6 +1415,32 @@ hipError_t launch_prepass(const AttnParams& p, uint16_t* v_t, const QuantParams*
 hipError_t launch_plan(const PlanBuild& pb, hipStream_t s) {
   hipLaunchKernelGGL(plan_kernel, dim3(pb.nb), dim3(256), 0, s, pb);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- static scratch
+// The workspace of attn_forward_noalloc, for callers that cannot allocate: a file-scope
+// device array that every GPU the library runs on holds until the process ends.  In host
+// code its name is only a stand-in for the symbol; the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_region(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------- MFMA throughput probe

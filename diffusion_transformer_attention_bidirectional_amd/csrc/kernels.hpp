@@ -109,6 +109,10 @@ hipError_t launch_q_codes(const QuantParams& p, int8_t* q_codes, hipStream_t s);
 hipError_t launch_int8_scores(const AttnParams& p, const int32_t* tiles, int n_tiles, int32_t* out,
                               bool bf16, hipStream_t s);
 hipError_t launch_mask_counts(const AttnParams& p, int mode, int32_t* out, hipStream_t s);
+// The library's static device scratch (the workspace of attn_forward_noalloc): its size,
+// and its address on the current device (looked up once per device).
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+hipError_t scratch_region(void** ptr);
 // kind 0 bf16, 1 f16 (32x32x16), 2 i8 (32x32x32); 512 threads per workgroup
 hipError_t launch_mfma_probe(int kind, int workgroups, int iters, float* sink, hipStream_t s);
 

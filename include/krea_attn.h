@@ -32,10 +32,10 @@
  *     aligned and strides multiples of 8 elements.
  *   - The caller owns q, k, v, o, the workspace and the stream.  Device entry points
  *     only enqueue work on the given HIP stream (NULL = the null stream) and return
- *     without synchronising.  attn_forward and attn_forward_gated allocate no device or
- *     pinned memory, copy nothing from the host and never wait for the device: they
- *     enqueue kernel launches only, so a call can be captured into a HIP graph, also its
- *     first call of a shape.
+ *     without synchronising.  attn_forward, attn_forward_gated and attn_forward_noalloc
+ *     allocate no device or pinned memory, copy nothing from the host and never wait for
+ *     the device: they enqueue kernel launches only, so a call can be captured into a HIP
+ *     graph, also its first call of a shape.
  *   - Plans: the library keeps a host-only cache of at most 8 plans ("Krea 2 Scanline
  *     Attention", "Where people get burned": masks cached by prompt length and
  *     resolution), keyed by every shape and mode argument: the logical layout, counts,
@@ -134,6 +134,22 @@ attn_status attn_workspace_bytes(const attn_args* args, size_t* bytes);
 attn_status attn_forward(const attn_args* args, const attn_tensor* q, const attn_tensor* k,
                          const attn_tensor* v, const attn_tensor* o, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* attn_forward for callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid device allocation): the same call with no workspace
+ * argument.  Its workspace is the library's static device scratch, a file-scope array of
+ * 128 MiB (134217728 bytes) that each GPU the library runs on holds until the process ends;
+ * that covers the 4 MP Krea shape (16896 tokens, 48 / 12 heads) in every mode.  A call
+ * whose attn_workspace_bytes() exceeds it returns ATTN_ERR_WORKSPACE before any device
+ * work.  Every call on one GPU shares that GPU's scratch, and each call overwrites what
+ * it uses (the split tail's counters are cleared by the call's own pre-pass kernel, not
+ * by a memset): calls that overlap on one GPU -- on different streams, or from different
+ * threads without ordering -- race and give undefined results.  Calls in one stream are
+ * ordered and safe.  No allocation, host copy or synchronisation, as attn_forward; the
+ * first call on a device looks up the scratch's address there (hipGetSymbolAddress).
+ * Arguments and errors otherwise as attn_forward. */
+attn_status attn_forward_noalloc(const attn_args* args, const attn_tensor* q, const attn_tensor* k,
+                                 const attn_tensor* v, const attn_tensor* o, void* stream);
 
 /* The attention call with the block's attention gate applied as the output is stored
  * ("LayerStream: Krea2 Chunking", "What the node does to the block": pass two computes the
