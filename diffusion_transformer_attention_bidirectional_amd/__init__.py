@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libkrea_attn.so")
 
 ATTN_F16, ATTN_BF16, ATTN_F32 = 0, 1, 2
 MODES = {"dense": 0, "tilemix": 1, "scanline": 2}
-PATTERNS = {"zero": 0, "one": 1, "band": 2, "all": 3}
+PATTERNS = {"zero": 0, "one": 1, "band": 2, "all": 3, "sage": 4}
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported dtype", -3: "unsupported shape",
           -4: "workspace too small", -5: "device error"}
 

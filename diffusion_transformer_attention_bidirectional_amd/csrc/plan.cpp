@@ -79,8 +79,8 @@ attn_status validate_args(const attn_args& a, std::string& err) {
   }
   if (a.mode == ATTN_TILEMIX) {
     if (a.pattern != ATTN_PAT_ZERO && a.pattern != ATTN_PAT_ONE && a.pattern != ATTN_PAT_BAND &&
-        a.pattern != ATTN_PAT_ALL) {
-      err = "pattern must be ATTN_PAT_ZERO, ATTN_PAT_ONE, ATTN_PAT_BAND or ATTN_PAT_ALL";
+        a.pattern != ATTN_PAT_ALL && a.pattern != ATTN_PAT_SAGE) {
+      err = "pattern must be ATTN_PAT_ZERO, ATTN_PAT_ONE, ATTN_PAT_BAND, ATTN_PAT_ALL or ATTN_PAT_SAGE";
       return ATTN_ERR_INVALID_ARG;
     }
     if (!(a.percentage >= 0.0 && a.percentage <= 1.0)) {
@@ -243,17 +243,23 @@ RouteRule route_rule(const attn_args& a, const Layout& lay, int64_t* n_int8) {
     r.kind = kRouteImage;
     const int64_t img = std::max(0, nb - r.text_blocks);
     count = img * img;
-  } else if (a.pattern == ATTN_PAT_BAND) {
-    // the candidates are the image-image tiles outside the band; the k smallest by
-    // (SplitMix64 key, a, b) go INT8, k = floor(percentage * candidates)
+  } else if (a.pattern == ATTN_PAT_BAND || a.pattern == ATTN_PAT_SAGE) {
+    // the band candidates are the image-image tiles outside the band; the k smallest by
+    // (SplitMix64 key, a, b) go INT8, k = floor(percentage * candidates).  The sage
+    // pattern keeps that k and draws the k smallest from every tile instead.
     std::vector<std::tuple<uint64_t, int, int>> cand;
     for (int qa = r.text_blocks; qa < nb; ++qa)
       for (int kb = r.text_blocks; kb < nb; ++kb)
         if (std::abs(qa - kb) > a.band_blocks) cand.emplace_back(route_key(a.seed, qa, kb), qa, kb);
     const int64_t k = (int64_t)std::floor(a.percentage * (double)cand.size());
+    if (a.pattern == ATTN_PAT_SAGE) {
+      cand.clear();
+      for (int qa = 0; qa < nb; ++qa)
+        for (int kb = 0; kb < nb; ++kb) cand.emplace_back(route_key(a.seed, qa, kb), qa, kb);
+    }
     if (k > 0) {
       std::nth_element(cand.begin(), cand.begin() + (k - 1), cand.end());
-      r.kind = kRouteBand;
+      r.kind = a.pattern == ATTN_PAT_SAGE ? kRoutePick : kRouteBand;
       r.thr_key = std::get<0>(cand[(size_t)(k - 1)]);
       r.thr_a = std::get<1>(cand[(size_t)(k - 1)]);
       r.thr_b = std::get<2>(cand[(size_t)(k - 1)]);

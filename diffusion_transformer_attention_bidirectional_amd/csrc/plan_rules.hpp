@@ -38,7 +38,9 @@ KREA_HD uint64_t route_key(uint64_t seed, int a, int b) {
 // How a TileMix call routes its tiles.  kRouteBand: the band-pattern candidates (image-image
 // tiles with |a - b| > band) whose (key, a, b) is at most the threshold tuple -- the k-th
 // smallest over all candidates, found once on the host -- are INT8: exactly the k smallest.
-enum { kRouteNone = 0, kRouteAll = 1, kRouteImage = 2, kRouteBand = 3 };
+// kRoutePick: the same threshold test over every tile, text and band included (the
+// comparison pattern that quantizes without regard to text, at the band's INT8 budget).
+enum { kRouteNone = 0, kRouteAll = 1, kRouteImage = 2, kRouteBand = 3, kRoutePick = 4 };
 struct RouteRule {
   int kind = kRouteNone;
   int band = 0;         // band half-width in blocks
@@ -50,10 +52,12 @@ struct RouteRule {
 
 KREA_HD bool route_is_int8(const RouteRule& r, int a, int b) {
   if (r.kind == kRouteAll) return true;
-  if (r.kind == kRouteNone || a < r.text_blocks || b < r.text_blocks) return false;
-  if (r.kind == kRouteImage) return true;
-  const int d = a > b ? a - b : b - a;
-  if (d <= r.band) return false;
+  if (r.kind != kRoutePick) {
+    if (r.kind == kRouteNone || a < r.text_blocks || b < r.text_blocks) return false;
+    if (r.kind == kRouteImage) return true;
+    const int d = a > b ? a - b : b - a;
+    if (d <= r.band) return false;
+  }
   const uint64_t key = route_key(r.seed, a, b);
   if (key != r.thr_key) return key < r.thr_key;
   return a != r.thr_a ? a < r.thr_a : b <= r.thr_b;

@@ -70,7 +70,7 @@ enum {
 
 enum { ATTN_F16 = 0, ATTN_BF16 = 1, ATTN_F32 = 2 };
 enum { ATTN_DENSE = 0, ATTN_TILEMIX = 1, ATTN_SCANLINE = 2 };
-enum { ATTN_PAT_ZERO = 0, ATTN_PAT_ONE = 1, ATTN_PAT_BAND = 2, ATTN_PAT_ALL = 3 };
+enum { ATTN_PAT_ZERO = 0, ATTN_PAT_ONE = 1, ATTN_PAT_BAND = 2, ATTN_PAT_ALL = 3, ATTN_PAT_SAGE = 4 };
 
 typedef struct {
   void* ptr;        /* device pointer to element [0, 0, 0, 0] */
@@ -95,7 +95,10 @@ typedef struct {
                            ATTN_PAT_BAND (diagonal band FP16, percentage of the rest INT8),
                            ATTN_PAT_ALL (every tile INT8, text included: the comparison
                            baseline of "What speedup to expect", a kernel that quantizes the
-                           text tiles too) */
+                           text tiles too), ATTN_PAT_SAGE (that baseline at the band's INT8
+                           budget: as many INT8 tiles as ATTN_PAT_BAND with the same
+                           percentage and band_blocks, the seeded pick drawn from every tile,
+                           text included) */
   double percentage;    /* in [0, 1]: share of the image-image tiles outside the band sent to INT8;
                            count = floor(percentage * candidates) */
   int32_t band_blocks;  /* band half-width w >= 0 in 128-token blocks: |a - b| <= w stays FP16 */

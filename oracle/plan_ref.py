@@ -62,7 +62,10 @@ def route_map(tokens: int, text_tokens: int, pattern: str, percentage: float = 0
 
     TileMix page, "What it actually patches" and "The inputs that matter".  Pattern "all"
     is the comparison baseline of the same page's "What speedup to expect": every tile
-    INT8, text tiles included, as in a kernel that quantizes the text tiles too.
+    INT8, text tiles included, as in a kernel that quantizes the text tiles too.  Pattern
+    "sage" is that comparison at the same INT8 budget: as many INT8 tiles as "band" with
+    the same percentage and band width, the seeded pick drawn from all tiles, text
+    included.
     """
     nb = n_blocks(tokens)
     r = np.zeros((nb, nb), dtype=np.uint8)
@@ -77,10 +80,15 @@ def route_map(tokens: int, text_tokens: int, pattern: str, percentage: float = 0
             for b in image:
                 r[a, b] = 1
         return r
-    if pattern != "band":
+    if pattern not in ("band", "sage"):
         raise ValueError(f"unknown pattern {pattern!r}")
     candidates = [(a, b) for a in image for b in image if abs(a - b) > band_blocks]
     k = math.floor(float(percentage) * len(candidates))
+    if pattern == "sage":
+        # the same INT8 budget as "band", drawn from every tile: a kernel that quantizes
+        # tiles without regard to text (the comparison of "What speedup to expect", at the
+        # same INT8 budget)
+        candidates = [(a, b) for a in range(nb) for b in range(nb)]
     seed &= _M64
     ranked = sorted(candidates, key=lambda ab: (splitmix64(seed ^ ((ab[0] << 32) | ab[1])), ab[0], ab[1]))
     for a, b in ranked[:k]:

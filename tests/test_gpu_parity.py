@@ -88,6 +88,8 @@ SMALL = [
                        img_rows=9, img_cols=30)),
     ("dense_scale", _w(softmax_scale=0.05, offset_std=0.0)),
     ("tilemix_all", _w(mode="tilemix", pattern="all", smooth_k=True, text_tokens=130, img_rows=12, img_cols=40)),
+    ("tilemix_sage", _w(mode="tilemix", pattern="sage", percentage=0.6, band_blocks=1, smooth_k=True,
+                        text_tokens=130, img_rows=16, img_cols=40)),
 ]
 
 
@@ -347,6 +349,7 @@ PLAN_CASES = [
                      seed=77)),
     ("tilemix", dict(text_tokens=100, img_rows=8, img_cols=50, pattern="one")),
     ("tilemix", dict(text_tokens=130, img_rows=12, img_cols=40, pattern="all")),
+    ("tilemix", dict(text_tokens=512, img_rows=64, img_cols=64, pattern="sage", percentage=0.5, band_blocks=2)),
     ("tilemix", dict(text_tokens=0, img_rows=300, img_cols=100, pattern="band", percentage=0.3, band_blocks=0,
                      seed=5)),
     ("scanline", dict(text_tokens=512, img_rows=64, img_cols=64, window=11, tile_aligned=True)),
@@ -462,23 +465,23 @@ def test_growing_key_norms(dev, mode):
 
 
 def test_int8_baseline_on_text_outliers(dev):
-    """The kernel against the oracle in the TileMix band pattern and in the all-INT8
-    baseline, on inputs with large text tokens and an outlier K channel ("What speedup to
-    expect"): each matches the oracle of its own routing, and quantizing the text tiles
-    costs far more error against exact attention."""
+    """The kernel against the oracle in the TileMix band pattern, the same-budget pick over
+    all tiles ('sage') and the all-INT8 baseline, on inputs with large text tokens and an
+    outlier K channel ("What speedup to expect"): each matches the oracle of its own routing,
+    and quantizing text tiles costs more error against exact attention."""
     w = _w(heads_q=4, heads_kv=1, mode="tilemix", pattern="band", percentage=0.5, band_blocks=1, smooth_k=True,
            text_tokens=128, img_rows=16, img_cols=32, seed=21)
     q, k, v = text_outlier_case(w)
     qd, kd, vd = to_f64(q), to_f64(k), to_f64(v)
     exact = attn_ref.attention(qd, kd, vd, w.with_(pattern="zero", smooth_k=False))
     rel = {}
-    for pattern in ("band", "all"):
+    for pattern in ("band", "sage", "all"):
         wp = w.with_(pattern=pattern)
         got, _ = _run(wp, dev, q, k, v)
         _assert_close(got, attn_ref.attention(qd, kd, vd, wp), f"{pattern} vs its oracle")
         rel[pattern] = float(np.sqrt(np.mean((got - exact) ** 2) / np.mean(exact ** 2)))
     print("rel RMS error against exact attention:", rel)
-    assert rel["all"] > 10.0 * rel["band"]
+    assert rel["all"] > 10.0 * rel["band"] and rel["sage"] > rel["band"]
 
 
 # ----------------------------------------------------------------------------- block context

@@ -75,6 +75,10 @@ ROUTE_CASES = [
     (5000, 77, "band", 0.2, 3, 99),
     (1500, 200, "all", 0.5, 2, 0),
     (4608, 512, "all", 0.0, 0, 1),
+    (4608, 512, "sage", 0.5, 2, 0),
+    (16896, 512, "sage", 0.75, 2, 0),
+    (1500, 200, "sage", 0.37, 1, 12345),
+    (300, 0, "sage", 0.9, 0, 2**63 + 5),
 ]
 
 

@@ -43,3 +43,40 @@ def test_tilemix_band_beats_all_int8_on_text_outliers(seed):
     assert rel_band <= rel_one
     assert rel_all > 2.0 * rel_one
     assert max_all > 2.0 * max_one
+
+
+SWEEP = [  # text_scale, outlier value; None: plain N(0, 1) inputs
+    None, (1.0, 8.0), (1.5, 6.0), (2.0, 8.0), (4.0, 24.0)]
+
+
+@pytest.mark.slow
+def test_band_against_same_budget_pick_over_all_tiles():
+    """The page's comparison at the same INT8 budget ("What speedup to expect": lower error
+    than a kernel that quantizes the text tiles too, at the same INT8 budget), at the 1 MP
+    token layout (512 text + 64 x 64 image tokens, 36 blocks; 4 query heads over 1 KV head):
+    'band' (w 2, 50 %) keeps text tiles and the diagonal band FP16 and sends 435 image tiles to
+    INT8; 'sage' sends the same 435 tiles to INT8, drawn from every tile.  Relative RMS error
+    against exact fp64 attention, on plain N(0, 1) inputs and with text tokens scaled and
+    carrying an outlier K channel of growing strength, tabulated.  With no outliers the two
+    are equal; the ratio grows with the outliers, through the page's 2-3x."""
+    from synth import make_qkv
+    w = Workload(name="adv", batch=1, heads_q=4, heads_kv=1, head_dim=128, text_tokens=512, img_rows=64,
+                 img_cols=64, dtype="bf16", seed=21, offset_std=0.5, mode="tilemix", pattern="band", percentage=0.5,
+                 band_blocks=2, smooth_k=True)
+    ratios = []
+    print("\ntext scale  outlier  band rel RMS  sage rel RMS  sage / band")
+    for setting in SWEEP:
+        q, k, v = make_qkv(w) if setting is None else text_outlier_case(w, text_scale=setting[0],
+                                                                         outlier_value=setting[1])
+        qd, kd, vd = to_f64(q), to_f64(k), to_f64(v)
+        exact = attn_ref.attention(qd, kd, vd, w.with_(pattern="zero", smooth_k=False))
+        rel = {}
+        for pattern in ("band", "sage"):
+            d = attn_ref.attention(qd, kd, vd, w.with_(pattern=pattern)) - exact
+            rel[pattern] = float(np.sqrt(np.mean(d ** 2) / np.mean(exact ** 2)))
+        ratios.append(rel["sage"] / rel["band"])
+        label = "N(0, 1) inputs     " if setting is None else f"{setting[0]:10.1f}  {setting[1]:7.1f}"
+        print(f"{label}  {rel['band']:12.3e}  {rel['sage']:12.3e}  {ratios[-1]:10.2f}")
+    assert abs(ratios[0] - 1.0) < 0.1
+    assert all(b > a for a, b in zip(ratios, ratios[1:]))
+    assert ratios[-1] > 10.0

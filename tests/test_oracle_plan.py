@@ -231,3 +231,29 @@ def test_scanline_counts_closed_form_4mp():
     # whole rows per tile: the exact rule and tile_aligned admit the same pairs, all tiles full
     assert set(np.unique(bm)) <= {0, 1}
     assert (plan_ref.block_mask(t, rows, cols, window, tile_aligned=False) == bm).all()
+
+
+@pytest.mark.parametrize("tokens,text,pct,w,seed", [(4608, 512, 0.5, 2, 0), (1500, 200, 0.37, 1, 12345),
+                                                    (1100, 130, 0.4, 1, 99)])
+def test_sage_pick_same_budget_any_tile_brute_force(tokens, text, pct, w, seed):
+    """The 'sage' pattern: exactly as many INT8 tiles as 'band' with the same percentage and
+    band width, the k smallest (key, a, b) over every tile, text and band included."""
+    band = plan_ref.route_map(tokens, text, "band", pct, w, seed)
+    sage = plan_ref.route_map(tokens, text, "sage", pct, w, seed)
+    assert int(sage.sum()) == int(band.sum())
+    nb = plan_ref.n_blocks(tokens)
+    keys = sorted((plan_ref.splitmix64(seed ^ (a << 32 | b)), a, b) for a in range(nb) for b in range(nb))
+    chosen = set((a, b) for _, a, b in keys[:int(band.sum())])
+    assert set(zip(*map(list, np.nonzero(sage)))) == chosen
+
+
+def test_sage_pick_reaches_text_and_band_tiles():
+    # at the 1 MP Krea shape (4 text blocks of 36) the same-budget pick over all tiles sends
+    # text tiles and band tiles to INT8, which the band pattern never does
+    sage = plan_ref.route_map(4608, 512, "sage", 0.5, 2, 0)
+    text = np.zeros_like(sage, dtype=bool)
+    text[:4, :] = True
+    text[:, :4] = True
+    a, b = np.indices(sage.shape)
+    assert int(sage[text].sum()) > 0 and int(sage[np.abs(a - b) <= 2].sum()) > 0
+    assert int(sage.sum()) == 435
