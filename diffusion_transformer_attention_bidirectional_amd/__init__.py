@@ -20,7 +20,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkrea_attn.so")
+# KREA_ATTN_LIB selects another build of the same library (the host-sanitizer build)
+LIB_PATH = os.environ.get("KREA_ATTN_LIB") or os.path.join(_HERE, "libkrea_attn.so")
 
 ATTN_F16, ATTN_BF16, ATTN_F32 = 0, 1, 2
 MODES = {"dense": 0, "tilemix": 1, "scanline": 2}

@@ -74,6 +74,52 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SAN_DIR = os.path.join(BUILD, "san")
+SAN_LIB = os.path.join(SAN_DIR, "libkrea_attn_san.so")
+# Host-only checking build: the planner, the C ABI and the GEMM glue built by the host
+# compiler with AddressSanitizer and UndefinedBehaviorSanitizer; the kernels unit is built
+# as usual (no GPU code is instrumented).  Load it with KREA_ATTN_LIB=<path> and the
+# sanitizer runtime preloaded (see sanitize_env()).
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=undefined", "-g", "-O1"]
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    os.makedirs(SAN_DIR, exist_ok=True)
+    gxx = shutil.which("g++") or "g++"
+    objs = []
+    for src in ("plan.cpp", "capi.cpp", "gemm.cpp"):
+        obj = os.path.join(SAN_DIR, src + ".o")
+        _run([gxx, "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC, "-I", "/opt/rocm/include",
+              "-D__HIP_PLATFORM_AMD__"] + SAN_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    kobj = os.path.join(SAN_DIR, "kernels.hip.o")
+    _run([hipcc()] + COMMON + DEVICE + ["-c", os.path.join(CSRC, "kernels.hip"), "-o", kobj])
+    _run([gxx, "-shared", "-o", SAN_LIB] + objs + [kobj] + SAN_FLAGS[:1] +
+         ["-L/opt/rocm/lib", "-lamdhip64", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"])
+    if verbose:
+        print("built", SAN_LIB)
+    return SAN_LIB
+
+
+def sanitize_env() -> dict:
+    """Environment that runs Python with the sanitized library: the sanitizer runtimes
+    preloaded (Python itself is not instrumented), leak checks off (the interpreter's own
+    allocations at exit are not the library's)."""
+    gxx = shutil.which("g++") or "g++"
+    libs = [subprocess.run([gxx, f"-print-file-name={n}"], capture_output=True, text=True).stdout.strip()
+            for n in ("libasan.so", "libubsan.so")]
+    env = dict(os.environ)
+    env.update(LD_PRELOAD=":".join(libs), KREA_ATTN_LIB=SAN_LIB,
+               ASAN_OPTIONS="detect_leaks=0:halt_on_error=1", UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    return env
+
+
 if __name__ == "__main__":
+    if len(sys.argv) > 1 and sys.argv[1] == "--sanitize":
+        build_sanitized(verbose=True)
+        # the host ABI tests against the sanitized library
+        r = subprocess.run([sys.executable, "-m", "pytest", "-q", os.path.join(ROOT, "tests", "test_host_abi.py")],
+                           env=sanitize_env(), cwd=ROOT)
+        sys.exit(r.returncode)
     build(verbose=True)
     sys.exit(0)
