@@ -214,6 +214,7 @@ struct Prepared {
   krea::WorkspaceLayout w;
   krea::TailRule tail;
   attn_args a;
+  int kmode = ATTN_DENSE;  // the attention kernel's mode
   hipStream_t st = nullptr;
   bool bf16 = true;
   int length = 0, chunk = 0;
@@ -279,6 +280,9 @@ attn_status prepare(const attn_args* args, const attn_tensor* q, const attn_tens
   out->w = w;
   out->tail = krea::tail_rule(a, plan.lay, a.mode != ATTN_SCANLINE ? cu_count() : 0, w.tail_parts);
   out->a = a;
+  // TileMix with no INT8 tile is dense attention: the dense kernel runs it (pattern zero is
+  // bit-identical to dense)
+  out->kmode = (a.mode == ATTN_TILEMIX && plan.int8_tiles == 0) ? ATTN_DENSE : a.mode;
   out->st = st;
   out->bf16 = bf16;
   out->length = plan.lay.length;
@@ -312,7 +316,7 @@ void set_launch(Prepared& pr, int slice) {
 
 attn_status launch_slice(Prepared& pr, int slice) {
   set_launch(pr, slice);
-  return hip_check(krea::launch_attention(pr.p, pr.a.mode, pr.bf16, pr.st), "attention launch");
+  return hip_check(krea::launch_attention(pr.p, pr.kmode, pr.bf16, pr.st), "attention launch");
 }
 
 attn_status forward_impl(const attn_args* args, const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,

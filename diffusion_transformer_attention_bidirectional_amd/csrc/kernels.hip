@@ -365,9 +365,10 @@ template <int MODE>
 __device__ __forceinline__ WorkItem work_item(const AttnParams& p, int n_hg) {
   const LaunchItem li = launch_item(MODE == kModeScan, p.lsplit, p.split, p.n_long, blockIdx.x);
   WorkItem w;
+  const u32 bq = li.j / (u32)n_hg;
   w.qt = (int)li.qt;
-  w.hg = (int)(li.j % n_hg);
-  w.b = (int)(li.j / n_hg);
+  w.hg = (int)(li.j - bq * (u32)n_hg);
+  w.b = (int)bq;
   w.part = li.part;
   w.nparts = li.nparts;
   w.slot = li.slot;

@@ -118,17 +118,22 @@ KREA_HD int scan_tile_class(const ScanGeom& g, const TileSpan& Q, const TileSpan
   return full ? 1 : 2;
 }
 
+// The launch-shape rules below run at the start of every attention workgroup, so they use
+// 32-bit unsigned arithmetic (a launch has fewer than 2^32 workgroups): 64-bit division is
+// a long software sequence on the GPU.
+typedef uint32_t u32;
+
 // XCD-contiguous remap: the hardware deals workgroups to the 8 XCDs round robin
 // (workgroup L to XCD L % 8); workgroup L = x + 8 i runs the i-th of XCD x's contiguous
 // range of the `total` items, so neighbouring items (one KV head's) share an L2.
-KREA_HD void xcd_range(int64_t total, int x, int64_t* base, int64_t* cnt) {
-  const int64_t per = total / 8, rem = total % 8;
+KREA_HD void xcd_range(u32 total, u32 x, u32* base, u32* cnt) {
+  const u32 per = total >> 3, rem = total & 7u;
   *base = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
   *cnt = x < rem ? per + 1 : per;
 }
-KREA_HD int64_t xcd_item(int64_t total, int64_t L) {
-  int64_t base, cnt;
-  xcd_range(total, (int)(L & 7), &base, &cnt);
+KREA_HD u32 xcd_item(u32 total, u32 L) {
+  u32 base, cnt;
+  xcd_range(total, L & 7u, &base, &cnt);
   return base + (L >> 3);
 }
 
@@ -137,23 +142,24 @@ KREA_HD int64_t xcd_item(int64_t total, int64_t L) {
 // others only their band.  Within each XCD's contiguous range, the text items run first,
 // then the others, each kind in item order, so that no long item starts late and leaves a
 // tail.  Returns the item workgroup L runs.
-KREA_HD int64_t scan_item_of(int64_t total, int64_t nq, int64_t n_long, int64_t L) {
-  int64_t base, cnt;
-  xcd_range(total, (int)(L & 7), &base, &cnt);
-  const int64_t idx = L >> 3;
-  const int64_t n_short = nq - n_long;
+KREA_HD u32 scan_item_of(u32 total, u32 nq, u32 n_long, u32 L) {
+  u32 base, cnt;
+  xcd_range(total, L & 7u, &base, &cnt);
+  const u32 idx = L >> 3;
+  const u32 n_short = nq - n_long;
   // long items among the first t: whole groups of nq, then the start of a partial group
-  auto longs_before = [&](int64_t t) {
-    const int64_t r = t % nq;
-    return (t / nq) * n_long + (r < n_long ? r : n_long);
-  };
-  const int64_t f0 = longs_before(base), nl = longs_before(base + cnt) - f0;
+  const u32 gb = base / nq, rb = base - gb * nq;
+  const u32 f0 = gb * n_long + (rb < n_long ? rb : n_long);
+  const u32 e = base + cnt, ge = e / nq, re = e - ge * nq;
+  const u32 nl = ge * n_long + (re < n_long ? re : n_long) - f0;
   if (idx < nl) {
-    const int64_t f = f0 + idx;  // global index among long items
-    return (f / n_long) * nq + f % n_long;
+    const u32 f = f0 + idx;  // global index among long items
+    const u32 g = f / n_long;
+    return g * nq + (f - g * n_long);
   }
-  const int64_t s = (base - f0) + (idx - nl);  // global index among short items
-  return (s / n_short) * nq + n_long + s % n_short;
+  const u32 s = (base - f0) + (idx - nl);  // global index among short items
+  const u32 g = s / n_short;
+  return g * nq + n_long + (s - g * n_short);
 }
 
 // Split tail.  With one attention workgroup per compute unit, the G items of a whole
@@ -171,54 +177,54 @@ struct TailRule {
 // The items of one launch over query tiles [qt_lo, qt_lo + nq) of every pair: per pair j,
 // tiles [0, u_j) run whole and [u_j, nq) split, u_j = uA for j < r and uB for j >= r.
 struct LaunchSplit {
-  int64_t J = 1, nq = 0;
-  int64_t r = 0, uA = 0, uB = 0;
-  int64_t n_full = 0, n_split = 0;  // whole items, split items
+  u32 J = 1, nq = 0;
+  u32 r = 0, uA = 0, uB = 0;
+  u32 n_full = 0, n_split = 0;  // whole items, split items
 };
 
 KREA_HD int64_t clamp64(int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 KREA_HD LaunchSplit launch_split(const TailRule& t, int64_t J, int64_t qt_lo, int64_t nq) {
   LaunchSplit s;
-  s.J = J;
-  s.nq = nq;
+  s.J = (u32)J;
+  s.nq = (u32)nq;
   if (t.split <= 1) {
     s.r = 0;
-    s.uA = s.uB = nq;
+    s.uA = s.uB = (u32)nq;
   } else {
     // first split tile of pair j: ceil((split_from - j) / J) = P + (j < r), split_from = P J + r
     const int64_t P = t.split_from / J;
-    s.r = t.split_from % J;
-    s.uA = clamp64(P + 1 - qt_lo, 0, nq);
-    s.uB = clamp64(P - qt_lo, 0, nq);
+    s.r = (u32)(t.split_from % J);
+    s.uA = (u32)clamp64(P + 1 - qt_lo, 0, nq);
+    s.uB = (u32)clamp64(P - qt_lo, 0, nq);
   }
-  s.n_full = s.r * s.uA + (J - s.r) * s.uB;
-  s.n_split = J * nq - s.n_full;
+  s.n_full = s.r * s.uA + (s.J - s.r) * s.uB;
+  s.n_split = s.J * s.nq - s.n_full;
   return s;
 }
 
 // The i-th whole item of a launch: (query tile within the launch, pair).
-KREA_HD void whole_item(const LaunchSplit& s, int64_t i, int64_t* qt, int64_t* j) {
-  const int64_t a = s.r * s.uA;
+KREA_HD void whole_item(const LaunchSplit& s, u32 i, u32* qt, u32* j) {
+  const u32 a = s.r * s.uA;
   if (i < a) {
     *j = i / s.uA;
-    *qt = i % s.uA;
+    *qt = i - *j * s.uA;
   } else {
-    const int64_t i2 = i - a;
-    *j = s.r + i2 / s.uB;
-    *qt = i2 % s.uB;
+    const u32 i2 = i - a, q = i2 / s.uB;
+    *j = s.r + q;
+    *qt = i2 - q * s.uB;
   }
 }
 // The i-th split item of a launch.
-KREA_HD void split_item(const LaunchSplit& s, int64_t i, int64_t* qt, int64_t* j) {
-  const int64_t sA = s.nq - s.uA, sB = s.nq - s.uB, a = s.r * sA;
+KREA_HD void split_item(const LaunchSplit& s, u32 i, u32* qt, u32* j) {
+  const u32 sA = s.nq - s.uA, sB = s.nq - s.uB, a = s.r * sA;
   if (i < a) {
     *j = i / sA;
-    *qt = s.uA + i % sA;
+    *qt = s.uA + (i - *j * sA);
   } else {
-    const int64_t i2 = i - a;
-    *j = s.r + i2 / sB;
-    *qt = s.uB + i2 % sB;
+    const u32 i2 = i - a, q = i2 / sB;
+    *j = s.r + q;
+    *qt = s.uB + (i2 - q * sB);
   }
 }
 
@@ -228,23 +234,23 @@ KREA_HD void split_item(const LaunchSplit& s, int64_t i, int64_t* qt, int64_t* j
 // also in XCD-contiguous ranges (the parts of one item, and the items of one KV head, on
 // one XCD).
 struct LaunchItem {
-  int64_t qt = 0, j = 0;
+  u32 qt = 0, j = 0;
   int part = 0, nparts = 1, slot = -1;  // slot: index of the item among the split ones
 };
-KREA_HD LaunchItem launch_item(bool scanline, const LaunchSplit& s, int split, int64_t n_long, int64_t L) {
+KREA_HD LaunchItem launch_item(bool scanline, const LaunchSplit& s, int split, u32 n_long, u32 L) {
   LaunchItem w;
   if (scanline) {
-    const int64_t t = scan_item_of(s.J * s.nq, s.nq, n_long, L);
-    w.qt = t % s.nq;
+    const u32 t = scan_item_of(s.J * s.nq, s.nq, n_long, L);
     w.j = t / s.nq;
+    w.qt = t - w.j * s.nq;
   } else if (L < s.n_full) {
     whole_item(s, xcd_item(s.n_full, L), &w.qt, &w.j);
   } else {
-    const int64_t t = xcd_item(s.n_split * split, L - s.n_full);
-    w.slot = (int)(t / split);
-    w.part = (int)(t - (int64_t)w.slot * split);
+    const u32 t = xcd_item(s.n_split * (u32)split, L - s.n_full);
+    w.slot = (int)(t / (u32)split);
+    w.part = (int)(t - (u32)w.slot * (u32)split);
     w.nparts = split;
-    split_item(s, w.slot, &w.qt, &w.j);
+    split_item(s, (u32)w.slot, &w.qt, &w.j);
   }
   return w;
 }
