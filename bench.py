@@ -13,7 +13,9 @@ torch.cuda.synchronize(); one JSON line on stdout.
 value = effective TFLOP/s = 4 * Hq * N^2 * d / time per call (dense-equivalent flops).
 roofline: the attention kernel's algorithmic flops per launch / its mean launch duration
 (HIP events on the stream the kernel runs on), against MI355X's dense bf16 MFMA peak; also
-against the rate the library's MFMA probe sustains on the same GPU (measured_mfma_peak).
+against the rates the library's MFMA probe sustains on the same GPU (measured_mfma_peak: on
+repeating operands, and for bf16 also on operands that change every product, as random data
+does; toggling operand bits draw more power, so the chip holds a lower clock).
 cpu_baseline: the fp64 numpy oracle on a bounded sample of the same workload (a few
 query heads), timed on this host's cores, scaled to TFLOP/s.
 detail: the same timing for the other Krea workloads (1 MP TileMix band, 1 MP scanline with
@@ -461,9 +463,9 @@ def main():
           flush=True)
     achieved = (head["bf16_flops"] + head["int8_ops"]) / (kern_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if head["int8_ops"] == 0 else roofline_peak_mixed(head["bf16_flops"], head["int8_ops"])
-    measured = {k: mfma_peak(dev, k) for k in ("bf16", "i8")}
-    print(f"# MFMA probe: bf16 {measured['bf16']:.0f} TFLOP/s, i8 {measured['i8']:.0f} TOPS sustained",
-          file=sys.stderr, flush=True)
+    measured = {k: mfma_peak(dev, k) for k in ("bf16", "i8", "bf16_random")}
+    print(f"# MFMA probe: bf16 {measured['bf16']:.0f} TFLOP/s ({measured['bf16_random']:.0f} on random operands), "
+          f"i8 {measured['i8']:.0f} TOPS sustained", file=sys.stderr, flush=True)
     detail = {}
     if not a.no_detail:
         for name in names[1:]:
@@ -513,11 +515,17 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": measured_traffic(a.workload),
                      "kernel": f"attn_fwd_kernel<bf16, {w.mode}>", "kernel_ms": round(kern_ms, 5),
                      "kernel_ms_median": round(kern_median_ms, 5),
-                     # the same kernel against the rate the MFMA probe sustains on this GPU
+                     # the same kernel against the rate the MFMA probe sustains on this GPU: on
+                     # operands that repeat, and (bf16) on operands that change every product,
+                     # which draw more power and hold a lower clock, as random data does
                      "measured_mfma_peak": {"bf16_tflops": round(measured["bf16"], 1),
+                                            "bf16_random_operands_tflops": round(measured["bf16_random"], 1),
                                             "i8_tops": round(measured["i8"], 1)},
                      "frac_of_measured_peak": round(
                          (head["bf16_flops"] / measured["bf16"] + head["int8_ops"] / measured["i8"]) / 1e12
+                         / (kern_ms * 1e-3), 4),
+                     "frac_of_random_operand_peak": round(
+                         (head["bf16_flops"] / measured["bf16_random"] + head["int8_ops"] / measured["i8"]) / 1e12
                          / (kern_ms * 1e-3), 4)},
         "plan_build_ms": round(head["plan_build_ms"], 3),
         # untimed calls before the K timed ones: at least --warmup and at least WARMUP_MS of work

@@ -247,7 +247,7 @@ def block_forward(x, wq, wk, wv, wg, wo, y, *, text_tokens, img_rows=0, img_cols
     return y
 
 
-PROBE_KINDS = {"bf16": 0, "f16": 1, "i8": 2}
+PROBE_KINDS = {"bf16": 0, "f16": 1, "i8": 2, "bf16_random": 3}
 
 
 def mfma_probe(kind: str, workgroups: int, iters: int, sink, stream=None) -> int:

@@ -696,7 +696,7 @@ attn_status attn_mask_row_counts(const attn_args* args, void* workspace, size_t 
 
 attn_status attn_mfma_probe(int32_t kind, int32_t workgroups, int32_t iters, void* sink, int64_t* ops,
                             void* stream) {
-  if (kind < ATTN_PROBE_BF16 || kind > ATTN_PROBE_I8) return fail(ATTN_ERR_INVALID_ARG, "unknown probe kind");
+  if (kind < ATTN_PROBE_BF16 || kind > ATTN_PROBE_BF16_RANDOM) return fail(ATTN_ERR_INVALID_ARG, "unknown probe kind");
   if (workgroups < 1 || iters < 1) return fail(ATTN_ERR_INVALID_ARG, "workgroups and iters must be >= 1");
   if (sink == nullptr || ops == nullptr) return fail(ATTN_ERR_INVALID_ARG, "sink and ops must not be NULL");
   const int64_t per_mfma = kind == ATTN_PROBE_I8 ? 2LL * 32 * 32 * 32 : 2LL * 32 * 32 * 16;

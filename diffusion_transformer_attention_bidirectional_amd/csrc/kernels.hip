@@ -1449,9 +1449,63 @@ hipError_t scratch_region(void** ptr) {
 // MFMA the attention kernel uses (bf16 / f16 32x32x16, i8 32x32x32), back to back, at the
 // attention kernel's occupancy (8 waves per workgroup, 2 per SIMD).  The operands depend on
 // the lane so nothing folds; the first thread stores a checksum of its accumulators, which
-// keeps every chain live and shows that the products ran.
+// keeps every chain live and shows that the products ran.  KIND 3 is the bf16 product on
+// operands that change from one product to the next (random signs and mantissas): the
+// matrix cores' power, and so the clock the chip holds, depends on how many operand bits
+// toggle, and the attention kernel's operands are random data.
+__device__ __forceinline__ uint32_t probe_hash(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+// Two bf16 values of magnitude in [0.5, 2) with random sign and mantissa.
+__device__ __forceinline__ uint32_t probe_pair(uint32_t h) {
+  return ((h & 0x807Fu) | 0x3F00u) | ((((h >> 16) & 0x807Fu) | 0x3F80u) << 16);
+}
+__device__ __forceinline__ uint4 probe_frag(uint32_t seed) {
+  return make_uint4(probe_pair(probe_hash(seed)), probe_pair(probe_hash(seed + 1)), probe_pair(probe_hash(seed + 2)),
+                    probe_pair(probe_hash(seed + 3)));
+}
+__device__ __forceinline__ void probe_random_bf16(int iters, float* sink) {
+  const uint32_t base = ((uint32_t)blockIdx.x * 512u + threadIdx.x) * 64u;
+  uint4 A[8], B[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    A[k] = probe_frag(base + 8 * k);
+    B[k] = probe_frag(base + 8 * k + 4);
+  }
+  f32x16 c0, c1, c2, c3;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) c0[r] = c1[r] = c2[r] = c3[r] = 0.f;
+  // four products per iteration, on fragments that rotate every iteration
+  int i = 0;
+  for (; i + 1 < iters; i += 2) {
+#pragma unroll
+    for (int k = 0; k < 8; k += 4) {
+      c0 = mma16<true>(A[k], B[k + 1], c0);
+      c1 = mma16<true>(A[k + 1], B[k + 2], c1);
+      c2 = mma16<true>(A[k + 2], B[k + 3], c2);
+      c3 = mma16<true>(A[k + 3], B[k], c3);
+    }
+  }
+  if (i < iters) {
+    c0 = mma16<true>(A[0], B[1], c0);
+    c1 = mma16<true>(A[1], B[2], c1);
+    c2 = mma16<true>(A[2], B[3], c2);
+    c3 = mma16<true>(A[3], B[0], c3);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) *(uint32_t*)sink = __float_as_uint(c0[0] + c1[1] + c2[2] + c3[3]);
+}
+
 template <int KIND>
 __global__ void __launch_bounds__(512) mfma_probe_kernel(int iters, float* sink) {
+  if (KIND == 3) {
+    probe_random_bf16(iters, sink);
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const uint32_t w = 0x3C003C00u ^ (uint32_t)(lane * 0x00010001u);
   const uint4 a = make_uint4(w, w ^ 1u, w ^ 2u, w ^ 3u), bv = make_uint4(w ^ 4u, w ^ 5u, w ^ 6u, w ^ 7u);
@@ -1485,7 +1539,8 @@ __global__ void __launch_bounds__(512) mfma_probe_kernel(int iters, float* sink)
 hipError_t launch_mfma_probe(int kind, int workgroups, int iters, float* sink, hipStream_t s) {
   if (kind == 0) hipLaunchKernelGGL(mfma_probe_kernel<0>, dim3(workgroups), dim3(512), 0, s, iters, sink);
   else if (kind == 1) hipLaunchKernelGGL(mfma_probe_kernel<1>, dim3(workgroups), dim3(512), 0, s, iters, sink);
-  else hipLaunchKernelGGL(mfma_probe_kernel<2>, dim3(workgroups), dim3(512), 0, s, iters, sink);
+  else if (kind == 2) hipLaunchKernelGGL(mfma_probe_kernel<2>, dim3(workgroups), dim3(512), 0, s, iters, sink);
+  else hipLaunchKernelGGL(mfma_probe_kernel<3>, dim3(workgroups), dim3(512), 0, s, iters, sink);
   return hipGetLastError();
 }
 

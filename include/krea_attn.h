@@ -284,14 +284,18 @@ attn_status attn_set_kernel_events(void* start_event, void* stop_event);
  * `workgroups` workgroups of 8 waves, the attention kernel's occupancy.  Each wave issues
  * 4 * iters independent MFMAs of `kind`:
  *   ATTN_PROBE_BF16, ATTN_PROBE_F16: 32x32x16 with fp32 accumulation;
- *   ATTN_PROBE_I8: 32x32x32 with int32 accumulation.
+ *   ATTN_PROBE_I8: 32x32x32 with int32 accumulation;
+ *   ATTN_PROBE_BF16_RANDOM: the bf16 product on operands that change from one product to
+ *   the next (random signs and mantissas, magnitudes in [0.5, 2)).  The matrix cores draw
+ *   more power, and the chip holds a lower clock, when more operand bits toggle, so this
+ *   is the rate to set beside a kernel whose operands are random data.
  * Timing the launch gives the rate the chip sustains for the products the attention
  * kernel is built from, to set beside the published dense peak.
  * - *ops (host pointer) receives the operations the launch performs (2 per multiply-add).
  * - sink: device memory of at least 4 bytes; receives a 32-bit checksum of the first
  *   wave's accumulators (the same for the same kind and iters).
  * workgroups >= 1 and iters >= 1; anything else is ATTN_ERR_INVALID_ARG.  Async on stream. */
-enum { ATTN_PROBE_BF16 = 0, ATTN_PROBE_F16 = 1, ATTN_PROBE_I8 = 2 };
+enum { ATTN_PROBE_BF16 = 0, ATTN_PROBE_F16 = 1, ATTN_PROBE_I8 = 2, ATTN_PROBE_BF16_RANDOM = 3 };
 attn_status attn_mfma_probe(int32_t kind, int32_t workgroups, int32_t iters, void* sink, int64_t* ops,
                             void* stream);
 

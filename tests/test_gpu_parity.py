@@ -546,7 +546,8 @@ def test_block_krea_1mp_sampled(dev):
     print(f"block 1mp sampled: max {mx:.2e} mean {mn:.2e} rel {rel:.2e}")
 
 
-@pytest.mark.parametrize("kind,per", [("bf16", 2 * 32 * 32 * 16), ("f16", 2 * 32 * 32 * 16), ("i8", 2 * 32 * 32 * 32)])
+@pytest.mark.parametrize("kind,per", [("bf16", 2 * 32 * 32 * 16), ("f16", 2 * 32 * 32 * 16), ("i8", 2 * 32 * 32 * 32),
+                                      ("bf16_random", 2 * 32 * 32 * 16)])
 def test_mfma_probe_runs_and_counts(dev, kind, per):
     """The MFMA throughput probe reports the operations of 4 * iters products per wave of 8
     waves per workgroup, and its products run: the accumulator checksum changes with iters

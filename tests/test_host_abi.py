@@ -302,7 +302,7 @@ def test_mfma_probe_validation(lib):
     """The probe rejects bad arguments before any device work (no GPU needed)."""
     ops = ctypes.c_int64(-7)
     sink = ctypes.c_void_p(0x100000)
-    assert lib.attn_mfma_probe(3, 1, 1, sink, ctypes.byref(ops), None) == -1
+    assert lib.attn_mfma_probe(4, 1, 1, sink, ctypes.byref(ops), None) == -1
     assert lib.attn_mfma_probe(-1, 1, 1, sink, ctypes.byref(ops), None) == -1
     assert lib.attn_mfma_probe(0, 0, 1, sink, ctypes.byref(ops), None) == -1
     assert lib.attn_mfma_probe(0, 1, 0, sink, ctypes.byref(ops), None) == -1
