@@ -24,7 +24,9 @@
 //     8*(r/4) + 4*(l/32) + r%4 (f32 and i32 results alike);
 //   * ds_read_tr16_b64: inside each group of 16 lanes, result lane i receives element
 //     i % 4 of the 8 bytes loaded by lanes i/4 + 4k of the group, k = 0..3;
-//   * global_load_lds (16 B): lane L writes LDS bytes [base + 16 L, +16).
+//   * global_load_lds (16 B): lane L writes LDS bytes [base + 16 L, +16), and the
+//     instruction counts in vmcnt only (an LDS read issued after it completes without
+//     waiting for it).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -200,6 +202,21 @@ __device__ __forceinline__ int k8_frag_off(int kb, int s, int lq, int lh) {
 
 __device__ __forceinline__ lds_void* as_lds(unsigned char* p) { return (lds_void*)p; }
 
+// One DMA instruction HBM -> LDS, 16 bytes per lane to LDS bytes [base + 16 lane, +16),
+// base wave-uniform.  Written as inline asm so that the compiler's wait-count model does
+// not see it: the model counts an LDS DMA as an LDS event that may complete out of order,
+// and while one is outstanding it can only wait for an LDS read with lgkmcnt(0), that is
+// for every LDS read in flight, before the first product of each region.  The hardware
+// counts the DMA in vmcnt alone.  Every reader of a staged tile runs after an explicit
+// s_waitcnt 0 (vmcnt included) and the workgroup barrier.  The instruction writes no
+// register, and M0 is declared clobbered.
+__device__ __forceinline__ void dma16(const void* src, unsigned char* dst) {
+  // the low 32 bits of a generic pointer into LDS are its LDS address
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(base)
+               : "memory", "m0");
+}
+
 // HBM -> LDS for one step, by DMA; 16 bytes per lane per instruction, 1 KB per
 // instruction (16 rows of one slab; 32 rows for INT8); the NW waves of the workgroup
 // share the instructions.  K of a full tile is 128 consecutive tokens of the tensor, so
@@ -227,7 +244,7 @@ __device__ __forceinline__ void dma_stage(const AttnParams& p, int b, int g, con
         const int n = wave * PER + i;
         const int row = (n & 7) * 16 + (lane >> 2);
         const uint32_t off = (uint32_t)row * (uint32_t)(p.k.st * 2) + (4 * (n >> 3) + ((lane & 3) ^ k_swz(row))) * 16;
-        __builtin_amdgcn_global_load_lds(kt + off, as_lds(stage + n * 1024), 16, 0, 0);
+        dma16(kt + off, stage + n * 1024);
       }
     } else {
 #pragma unroll
@@ -236,8 +253,7 @@ __device__ __forceinline__ void dma_stage(const AttnParams& p, int b, int g, con
         const int row = (n & 7) * 16 + (lane >> 2);
         const int t = s.k0 + row;
         const int ph = tok_valid<MODE>(p, t) ? tok_phys<MODE>(p, t) : 0;
-        __builtin_amdgcn_global_load_lds(kbase + ((int64_t)ph * p.k.st + (4 * (n >> 3) + ((lane & 3) ^ k_swz(row))) * 8) * 2,
-                                         as_lds(stage + n * 1024), 16, 0, 0);
+        dma16(kbase + ((int64_t)ph * p.k.st + (4 * (n >> 3) + ((lane & 3) ^ k_swz(row))) * 8) * 2, stage + n * 1024);
       }
     }
   }
@@ -248,7 +264,7 @@ __device__ __forceinline__ void dma_stage(const AttnParams& p, int b, int g, con
       const int n = wave * PER + i;
       const int d = (n & 7) * 16 + (lane >> 2);
       const uint32_t off = d * 256 + (4 * (n >> 3) + ((lane & 3) ^ k_swz(d))) * 16;
-      __builtin_amdgcn_global_load_lds(vt + off, as_lds(stage + V_OFF + n * 1024), 16, 0, 0);
+      dma16(vt + off, stage + V_OFF + n * 1024);
     }
   }
   if ((PARTS & 1) && MODE == kModeTileMix && s_int8) {
@@ -260,8 +276,7 @@ __device__ __forceinline__ void dma_stage(const AttnParams& p, int b, int g, con
       const int slab = n >> 2;
       const int row = (n & 3) * 32 + (lane >> 1);
       const int pc = lane & 1;
-      __builtin_amdgcn_global_load_lds(kc + row * 128 + (2 * slab + (pc ^ k8_swz(row))) * 16,
-                                       as_lds(stage + n * 1024), 16, 0, 0);
+      dma16(kc + row * 128 + (2 * slab + (pc ^ k8_swz(row))) * 16, stage + n * 1024);
     }
   }
 }

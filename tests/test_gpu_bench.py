@@ -33,6 +33,10 @@ def test_bench_json_contract():
     assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s" and roof["peak"] == 2500.0
     assert 0 < roof["frac"] < 1 and abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     assert roof["traffic"] is None or roof["traffic"] > 0
+    # the MFMA probe's rates: repeating operands, random bf16 operands (lower: a lower clock), i8
+    peak = roof["measured_mfma_peak"]
+    assert 0 < peak["bf16_random_operands_tflops"] <= peak["bf16_tflops"] * 1.02 and peak["i8_tops"] > 0
+    assert roof["frac_of_measured_peak"] <= roof["frac_of_random_operand_peak"] * 1.02
     cpu = r["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
 
