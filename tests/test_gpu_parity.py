@@ -101,6 +101,40 @@ def test_small_vs_oracle(dev, name, w):
     print(f"{name}: max {mx:.2e} mean {mn:.2e} rel {rel:.2e}")
 
 
+def _random_cases(count=30, seed=20261203):
+    """Seeded random shapes and mode arguments: dtype, batch, GQA ratio, text length, image
+    grid (ragged in both directions), mode, TileMix pattern / percentage / band / smooth_k,
+    scanline window / tile alignment, q_chunk."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(count):
+        hq, hkv = [(4, 1), (8, 2), (8, 1), (12, 3), (16, 2)][rng.integers(5)]
+        mode = ["dense", "tilemix", "scanline"][i % 3]
+        rows, cols = int(rng.integers(1, 25)), int(rng.integers(1, 65))
+        kw = dict(name=f"rand{i}", batch=int(rng.integers(1, 3)), heads_q=hq, heads_kv=hkv, head_dim=128,
+                  text_tokens=int(rng.integers(0, 401)), img_rows=rows, img_cols=cols,
+                  dtype=["bf16", "f16"][rng.integers(2)], seed=1000 + i, offset_std=0.5, mode=mode,
+                  q_chunk=[0, 128, 256][rng.integers(3)])
+        if mode == "tilemix":
+            kw.update(pattern=["band", "band", "one", "all", "sage", "zero"][rng.integers(6)],
+                      percentage=float(rng.uniform(0, 1)), band_blocks=int(rng.integers(0, 3)),
+                      smooth_k=bool(rng.integers(2)), route_seed=int(rng.integers(0, 1 << 31)))
+        elif mode == "scanline":
+            kw.update(window=int(2 * rng.integers(0, 8) + 1), tile_aligned=bool(rng.integers(2)))
+        cases.append(Workload(**kw))
+    return cases
+
+
+@pytest.mark.parametrize("w", _random_cases(), ids=lambda w: w.name)
+def test_random_shapes_vs_oracle(dev, w):
+    """Every element of a seeded random configuration against the oracle."""
+    got, (q, k, v) = _run(w, dev)
+    ref = attn_ref.attention(to_f64(q), to_f64(k), to_f64(v), w)
+    mx, mn, rel = _assert_close(got, ref, w.name)
+    print(f"{w.name} {w.mode} {w.dtype} B={w.batch} H={w.heads_q}/{w.heads_kv} N={w.text_tokens}+{w.img_rows}x"
+          f"{w.img_cols} chunk={w.q_chunk}: max {mx:.2e} mean {mn:.2e} rel {rel:.2e}", flush=True)
+
+
 @pytest.mark.parametrize("w", [
     _w(),
     _w(mode="tilemix", pattern="band", percentage=0.6, band_blocks=1, smooth_k=True, text_tokens=130,
