@@ -476,6 +476,12 @@ __device__ __forceinline__ f32x16 qk_scores_any(const unsigned char* __restrict_
   return qk_scores<BF16, false>(buf, kb, lq, lh, qf, q8f);
 }
 
+// Where the step forms the score minus the running max: TileMix in region A, beside the P V
+// products (same-box A/B: 4 MP band 0.6-1.0 % faster, 1 MP band within 0.3 %); dense and
+// scanline beside the exponentials in region B (region A measured 0.7-1.0 % slower there).
+template <int MODE>
+constexpr bool shift_in_a() { return MODE == kModeTileMix; }
+
 // Software pipeline over 32-key sub-blocks.  Sub-block j is handled in two scheduling
 // regions, so that every stretch of vector work has independent MFMAs beside it:
 //   A: O += V^T P^T of sub-block j - 1 (MFMA)   |  row max of S_j, lazy-rescale decision
@@ -491,15 +497,19 @@ struct Pipe {
   uint4 vf[2][4];  // V^T fragments of the previous sub-block
 };
 
-// P = exp2(S * mul + add - m) of one sub-block (S already masked and scaled on partial
-// tiles), packed as the P^T operand of the P V product, and the row sum of exactly those
-// rounded values.  The sum runs in two interleaved chains and is pinned to the calling
+// P = exp2(S * mul + add - m) of one sub-block, packed as the P^T operand of the P V
+// product, and the row sum of exactly those rounded values.  On partial tiles S is already
+// masked and scaled; with SHIFTED (shift_in_a) S already holds the log2-domain score minus
+// the running max.  The sum runs in two interleaved chains and is pinned to the calling
 // region: left alone, the compiler sinks the sums of all four sub-blocks into one
 // dependent chain at the end of the step.
-template <bool BF16, bool PARTIAL>
+template <bool BF16, bool PARTIAL, bool SHIFTED>
 __device__ __forceinline__ void probabilities(f32x16& S, float mul, float add, float alpha, Pipe& pp,
                                               WaveState& ws) {
-  if (PARTIAL) {
+  if (SHIFTED) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[r] = __builtin_amdgcn_exp2f(S[r]);
+  } else if (PARTIAL) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) S[r] = __builtin_amdgcn_exp2f(S[r] - ws.m);
   } else {
@@ -580,6 +590,18 @@ __device__ __forceinline__ void sub_block(const AttnParams& p, const unsigned ch
 #pragma unroll
       for (int r = 0; r < 16; ++r) ws.O[db][r] *= alpha;
   }
+  if (shift_in_a<MODE>()) {
+    // the log2-domain score minus the running max, here rather than beside the
+    // exponentials in region B
+    if (PARTIAL) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[r] -= ws.m;
+    } else {
+      const float c = add - ws.m;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[r] = fmaf(S[r], mul, c);
+    }
+  }
   if (LAST) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -595,14 +617,14 @@ __device__ __forceinline__ void sub_block(const AttnParams& p, const unsigned ch
     // faster on scanline, 0.8 % slower on dense, which keeps the shared tail)
     if (hn) {
       Sn = qk_scores_any<BF16, MODE>(nbuf, nxt_int8, 0, lq, lh, qf, q8f);
-      probabilities<BF16, PARTIAL>(S, mul, add, alpha, pp, ws);
+      probabilities<BF16, PARTIAL, shift_in_a<MODE>()>(S, mul, add, alpha, pp, ws);
     } else {
-      probabilities<BF16, PARTIAL>(S, mul, add, alpha, pp, ws);
+      probabilities<BF16, PARTIAL, shift_in_a<MODE>()>(S, mul, add, alpha, pp, ws);
     }
   } else {
     if (!LAST) Sn = qk_scores_any<BF16, MODE>(buf, int8, kb + 1, lq, lh, qf, q8f);
     else if (hn) Sn = qk_scores_any<BF16, MODE>(nbuf, nxt_int8, 0, lq, lh, qf, q8f);
-    probabilities<BF16, PARTIAL>(S, mul, add, alpha, pp, ws);
+    probabilities<BF16, PARTIAL, shift_in_a<MODE>()>(S, mul, add, alpha, pp, ws);
   }
   __builtin_amdgcn_s_setprio(0);
   __builtin_amdgcn_sched_barrier(0);
