@@ -320,11 +320,12 @@ def test_krea_1mp_full(dev, name, dtype):
     print(f"{name} {dtype}: max {mx:.2e} mean {mn:.2e} rel {rel:.2e}", flush=True)
 
 
-@pytest.mark.parametrize("name", ["4mp_dense", "4mp_band"])
+@pytest.mark.parametrize("name", ["4mp_dense", "4mp_band", "4mp_scanline"])
 def test_krea_4mp_one_head_per_group(dev, name):
-    """The 4 MP Krea shape (N = 16896; TileMix band 75 % with 4096-token query slices) against
-    the oracle on every row of one query head of each of the 12 KV groups, so every query tile
-    of every head group, the split tail's items among them, is compared element by element."""
+    """The 4 MP Krea shape (N = 16896; TileMix band 75 % with 4096-token query slices;
+    scanline with one 128-token tile per grid row, window 11) against the oracle on every row
+    of one query head of each of the 12 KV groups, so every query tile of every head group,
+    the split tail's items among them, is compared element by element."""
     w = WORKLOADS[name]
     got, (q, k, v) = _run(w, dev)
     ora = attn_ref.Oracle(to_f64(q), to_f64(k), to_f64(v), w)
