@@ -429,16 +429,16 @@ def test_device_plan_matches_oracle(dev, mode, kw):
         assert res["lists"][a, :len(row)].tolist() == row, a
 
 
-def test_krea_1mp_batch2_band_sampled(dev):
+def test_krea_1mp_batch2_band_full(dev):
     """Two samples at the 1 MP shape in TileMix band mode: batch strides, the per-sample
-    smooth_k mean and K codes, checked on sampled rows of the second sample."""
+    smooth_k mean and K codes, every element of both samples against the oracle."""
     w = WORKLOADS["1mp_band"].with_(batch=2)
     got, (q, k, v) = _run(w, dev)
-    ora = attn_ref.Oracle(to_f64(q), to_f64(k), to_f64(v), w)
-    rows = _sample_rows(w.tokens, w.text_tokens, np.random.default_rng(9), count=24)
-    for h in (1, 30):
-        ref = ora.rows(1, h, rows)
-        _assert_close(got[1, rows, h], ref, f"batch 2 head {h}")
+    print("1mp band batch 2: GPU done, oracle ...", flush=True)
+    ref = attn_ref.Oracle(to_f64(q), to_f64(k), to_f64(v), w).forward()
+    for b in range(2):
+        mx, mn, rel = _assert_close(got[b], ref[b], f"batch 2 sample {b}")
+        print(f"1mp band batch 2 sample {b}: max {mx:.2e} mean {mn:.2e} rel {rel:.2e}", flush=True)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
